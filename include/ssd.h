@@ -1,0 +1,166 @@
+/*
+ * ssd.h -- C ABI of libssd: the Mamba-2 state-space-duality (SSD) layer on one
+ * AMD Instinct MI355X (gfx950): chunked prefill scan and O(1) cached decode.
+ *
+ * The operation.  "Compiler-First State Space Duality and Portable O(1)
+ * Autoregressive Caching for Inference" (section 2, methodology) describes
+ * the SSD layer as a per-head diagonal state recurrence that is cut into
+ * fixed-size chunks and evaluated with einsum-style contractions and static
+ * causal (lower-triangular) masks, the decay being exponentiated in float32,
+ * and a fixed-size per-sequence state cache that decoding updates in place
+ * on the device (sections 2 and 3).  The page never writes the recurrence;
+ * this library computes the Mamba-2 SSD layer with a scalar-times-identity
+ * state matrix per head.  For batch row b, head h, group g = h / (H / G):
+ *
+ *     alpha_t = exp(dt[b,t,h] * A[h])
+ *     H_t     = alpha_t * H_{t-1} + dt[b,t,h] * x[b,t,h,:] (outer) B[b,t,g,:]
+ *     y[b,t,h,:] = H_t . C[b,t,g,:] + D[h] * x[b,t,h,:]
+ *
+ * H_t is the P x N state (headdim x dstate).  ssd_chunk_scan evaluates this
+ * for t = 1..L with the chunked (state-space-duality) algorithm: inside each
+ * chunk of Q tokens a causal quadratic form, across chunks a state passed from
+ * chunk to chunk.  ssd_decode_step is exactly one more step t on the cached
+ * state.  dt is taken as given (already softplus-ed, positive); A should be
+ * <= 0 (A > 0 is not rejected, but exp(dt*A) may overflow and is unsupported).
+ *
+ * Conventions shared by every call:
+ *   - Every tensor pointer is a DEVICE pointer to contiguous row-major memory
+ *     owned by the caller; the library allocates no device memory and keeps
+ *     no pointer after a call returns.
+ *   - stream is a hipStream_t passed as void* (NULL = the default stream).
+ *     Calls enqueue work asynchronously and return without synchronising.
+ *   - Arguments are validated before any device call; on an error nothing is
+ *     launched and a status code is returned.  No call aborts or throws.
+ *   - Alignment: x, B, C, y and the state / workspace buffers must be 16-byte
+ *     aligned (x and y of ssd_decode_step: element-aligned); dt, A, D 4-byte.
+ *     Otherwise SSD_ERR_ALIGNMENT.
+ *   - Float inputs must be finite.  Outputs for non-finite inputs are undefined.
+ *   - The library holds no global state; calls on different streams may run
+ *     concurrently if their buffers do not overlap.
+ *   - Shapes (x, y : [B, L, H, P] of io_dtype; dt : [B, L, H] fp32;
+ *     A, D : [H] fp32; B, C : [B, L, G, N] of io_dtype;
+ *     state : [B, H, P, N] fp32, n fastest).
+ */
+#ifndef SSD_H
+#define SSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_NULL = 1,        /* a required pointer is NULL                        */
+    SSD_ERR_SHAPE = 2,       /* a size is out of range, or nheads % ngroups != 0  */
+    SSD_ERR_UNSUPPORTED = 3, /* valid, but not an implemented (P, N, Q, dtype)    */
+    SSD_ERR_ALIAS = 4,       /* an output overlaps a buffer it must not overlap   */
+    SSD_ERR_WORKSPACE = 5,   /* workspace NULL or smaller than required           */
+    SSD_ERR_DEVICE = 6,      /* a HIP runtime call or kernel launch failed        */
+    SSD_ERR_ALIGNMENT = 7    /* a pointer is not aligned as required              */
+} ssd_status;
+
+typedef enum ssd_dtype {
+    SSD_F32 = 0,             /* x, B, C, y in float32                             */
+    SSD_BF16 = 1             /* x, B, C, y in bfloat16                            */
+} ssd_dtype;
+
+/* Problem sizes.  seqlen and chunk are ignored by ssd_decode_step and
+ * ssd_state_init.  reserved must be 0. */
+typedef struct ssd_dims {
+    int64_t batch;     /* B >= 0                                              */
+    int64_t seqlen;    /* L >= 0 tokens per sequence                          */
+    int64_t nheads;    /* H >= 1                                              */
+    int64_t headdim;   /* P >= 1                                              */
+    int64_t dstate;    /* N >= 1                                              */
+    int64_t ngroups;   /* G >= 1, H % G == 0; head h reads B/C group h/(H/G)  */
+    int64_t chunk;     /* Q >= 1, chunk length of the chunked scan            */
+    int32_t io_dtype;  /* ssd_dtype of x, B, C, y                             */
+    int32_t reserved;  /* must be 0                                           */
+} ssd_dims;
+
+/* Human-readable name of a status code (static storage; never NULL). */
+const char *ssd_status_string(ssd_status status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int ssd_version(void);
+
+/*
+ * ssd_state_init -- set the cached state of every (batch row, head).
+ *   state : [B, H, P, N] fp32, written.
+ *   src   : [B, H, P, N] fp32 to copy from, or NULL for the zero state
+ *           (the empty cache: H_0 = 0).  src == state is a no-op; any other
+ *           overlap of src and state returns SSD_ERR_ALIAS.
+ * Implemented with a fill/copy kernel (no hipMemsetAsync), so it may be
+ * captured in a HIP graph.  Section 2 of the page: the cache lives on the
+ * device and is initialised there.
+ */
+ssd_status ssd_state_init(const ssd_dims *dims, float *state, const float *src, void *stream);
+
+/*
+ * ssd_chunk_scan_workspace_size -- bytes of device workspace ssd_chunk_scan
+ * needs for these sizes (0 is possible).  *bytes is written on SSD_OK.  The
+ * result depends on dims only.
+ */
+ssd_status ssd_chunk_scan_workspace_size(const ssd_dims *dims, size_t *bytes);
+
+/*
+ * ssd_chunk_scan -- prefill: run the recurrence over L tokens of every
+ * sequence with the chunked algorithm of chunk length Q (section 2 of the
+ * page: chunked recurrence, static causal masks, float32 decay exponentials).
+ *   x [B,L,H,P], dt [B,L,H], A [H], B [B,L,G,N], C [B,L,G,N], D [H]   inputs
+ *   initial_state [B,H,P,N] fp32, or NULL for the zero state            input
+ *   y [B,L,H,P] (io_dtype)                                               output
+ *   final_state [B,H,P,N] fp32 = H_L                                     output
+ *   workspace : device buffer of >= ssd_chunk_scan_workspace_size bytes,
+ *               16-byte aligned; contents on entry are ignored.
+ * final_state may be the same pointer as initial_state (resume a cache in
+ * place); y must not overlap any input, the state buffers or the workspace.
+ * L need not be a multiple of Q (the last chunk is then shorter); L == 0
+ * writes final_state = initial_state (or zeros); B == 0 does nothing.
+ * Supported: io_dtype SSD_BF16 with (P, N) = (64, 128) and Q a multiple of
+ * 64 up to 512 (bf16 MFMA path, fp32 accumulation); io_dtype SSD_F32 with
+ * P <= 64, N <= 128, Q <= 256 (fp32 path).  Others: SSD_ERR_UNSUPPORTED.
+ */
+ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const float *dt, const float *A,
+                          const void *B, const void *C, const float *D,
+                          const float *initial_state, void *y, float *final_state,
+                          void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * ssd_decode_step -- one O(1) cached decode step for every sequence (section
+ * 2 of the page: the fixed-size on-device cache, updated per generated token
+ * with no host round trip; section 4: decode is bandwidth-bound).  Each
+ * state element is read once and written once, and y is reduced in the same
+ * pass.
+ *   x [B,H,P], dt [B,H], A [H], B [B,G,N], C [B,G,N], D [H]   one token per sequence
+ *   state [B,H,P,N] fp32, updated in place: H <- alpha*H + dt * x (outer) B
+ *   y [B,H,P] (io_dtype) = H_new . C + D * x
+ * y must not overlap the state or any input.  Supported: N in {16, 32, 64,
+ * 128, 256}, any P >= 1, io_dtype SSD_F32 or SSD_BF16.
+ */
+ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const float *dt, const float *A,
+                           const void *B, const void *C, const float *D, float *state, void *y,
+                           void *stream);
+
+/*
+ * ssd_chunk_scan_timed -- measurement entry point: the same computation as
+ * ssd_chunk_scan (same arguments and results), run synchronously; the device
+ * time of each kernel the scan launched is written to kernel_ms[0 ..
+ * *n_kernels-1] (HIP events on the given stream) and their names to
+ * kernel_names (static strings; may be NULL).  On input *n_kernels is the
+ * capacity of the arrays; on SSD_OK it is the number of kernels launched.
+ */
+ssd_status ssd_chunk_scan_timed(const ssd_dims *dims, const void *x, const float *dt,
+                                const float *A, const void *B, const void *C, const float *D,
+                                const float *initial_state, void *y, float *final_state,
+                                void *workspace, size_t workspace_bytes, void *stream,
+                                float *kernel_ms, const char **kernel_names, int *n_kernels);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSD_H */

@@ -1,0 +1,180 @@
+"""Python binding of libssd, the MI355X (gfx950) Mamba-2 SSD prefill scan and
+O(1) cached decode step.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of ``libssd.so`` (C ABI in ``include/ssd.h``).  PyTorch provides device
+memory and the stream.  There is no fallback: if the library is missing, or a
+call fails, an exception is raised.
+
+Functions keep the C names:
+    ssd_state_init(state, src=None)
+    ssd_chunk_scan_workspace_size(...)
+    ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, ...) -> (y, final_state)
+    ssd_decode_step(x, dt, A, B, C, D, state, y=None) -> y
+    ssd_chunk_scan_timed(...) -> (y, final_state, [(kernel, ms), ...])
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIBRARY = os.path.join(PKG, "libssd.so")
+
+SSD_F32, SSD_BF16 = 0, 1
+STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
+          4: "SSD_ERR_ALIAS", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_DEVICE", 7: "SSD_ERR_ALIGNMENT"}
+EXPORTS = ("ssd_status_string", "ssd_version", "ssd_state_init", "ssd_chunk_scan_workspace_size",
+           "ssd_chunk_scan", "ssd_decode_step", "ssd_chunk_scan_timed")
+
+
+class SsdError(RuntimeError):
+    def __init__(self, fn: str, code: int, msg: str):
+        super().__init__(f"{fn} failed: {msg}")
+        self.code = code
+
+
+class SsdDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("seqlen", ctypes.c_int64),
+                ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
+                ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
+                ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+_lib = None
+
+
+def load(path: str | None = None):
+    """Load libssd.so (built in-tree by ``state_space_model_mamba_amd.build``)."""
+    global _lib
+    if _lib is not None and path is None:
+        return _lib
+    p = path or LIBRARY
+    if not os.path.exists(p):
+        raise RuntimeError(f"libssd not built: {p} is missing "
+                           "(run `python -m state_space_model_mamba_amd.build`)")
+    lib = ctypes.CDLL(p)
+    vp, fp, i64p = ctypes.c_void_p, ctypes.c_void_p, ctypes.POINTER(ctypes.c_size_t)
+    dims = ctypes.POINTER(SsdDims)
+    lib.ssd_status_string.argtypes = [ctypes.c_int]
+    lib.ssd_status_string.restype = ctypes.c_char_p
+    lib.ssd_version.argtypes = []
+    lib.ssd_version.restype = ctypes.c_int
+    lib.ssd_state_init.argtypes = [dims, fp, fp, vp]
+    lib.ssd_state_init.restype = ctypes.c_int
+    lib.ssd_chunk_scan_workspace_size.argtypes = [dims, i64p]
+    lib.ssd_chunk_scan_workspace_size.restype = ctypes.c_int
+    lib.ssd_chunk_scan.argtypes = [dims] + [vp] * 10 + [ctypes.c_size_t, vp]
+    lib.ssd_chunk_scan.restype = ctypes.c_int
+    lib.ssd_chunk_scan_timed.argtypes = ([dims] + [vp] * 10 + [ctypes.c_size_t, vp] +
+                                         [ctypes.POINTER(ctypes.c_float),
+                                          ctypes.POINTER(ctypes.c_char_p),
+                                          ctypes.POINTER(ctypes.c_int)])
+    lib.ssd_chunk_scan_timed.restype = ctypes.c_int
+    lib.ssd_decode_step.argtypes = [dims] + [vp] * 9
+    lib.ssd_decode_step.restype = ctypes.c_int
+    if path is None:
+        _lib = lib
+    return lib
+
+
+def _check(fn: str, rc: int):
+    if rc != 0:
+        msg = load().ssd_status_string(rc).decode()
+        raise SsdError(fn, rc, msg)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream):
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _io_dtype(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise TypeError(f"x/B/C must be bfloat16 or float32, got {t.dtype}")
+
+
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype) -> SsdDims:
+    return SsdDims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype, 0)
+
+
+def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
+                                  io_dtype=SSD_BF16) -> int:
+    d = make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype)
+    n = ctypes.c_size_t(0)
+    _check("ssd_chunk_scan_workspace_size",
+           load().ssd_chunk_scan_workspace_size(ctypes.byref(d), ctypes.byref(n)))
+    return int(n.value)
+
+
+def ssd_state_init(state, src=None, stream=None):
+    """state [B, H, P, N] fp32 <- src (or zeros)."""
+    b, h, p, n = state.shape
+    d = make_dims(b, 0, h, p, n, 1, 1, SSD_F32)
+    _check("ssd_state_init", load().ssd_state_init(ctypes.byref(d), _ptr(state), _ptr(src),
+                                                   _stream(stream)))
+    return state
+
+
+def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace):
+    import torch
+    bsz, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    io = _io_dtype(x)
+    d = make_dims(bsz, L, H, P, N, G, chunk, io)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_state is None:
+        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
+    need = ssd_chunk_scan_workspace_size(bsz, L, H, P, N, G, chunk, io)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    args = [ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+            _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace), ws_bytes]
+    return args, y, final_state
+
+
+def ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_state=None,
+                   workspace=None, stream=None):
+    """Prefill over x[B, L, H, P]; returns (y, final_state)."""
+    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace)
+    _check("ssd_chunk_scan", load().ssd_chunk_scan(*args, _stream(stream)))
+    return y, fs
+
+
+def ssd_chunk_scan_timed(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_state=None,
+                         workspace=None, stream=None):
+    """As ssd_chunk_scan, synchronously, also returning [(kernel name, ms), ...]."""
+    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace)
+    cap = 8
+    ms = (ctypes.c_float * cap)()
+    names = (ctypes.c_char_p * cap)()
+    n = ctypes.c_int(cap)
+    _check("ssd_chunk_scan_timed", load().ssd_chunk_scan_timed(*args, _stream(stream), ms, names,
+                                                               ctypes.byref(n)))
+    return y, fs, [(names[i].decode(), float(ms[i])) for i in range(n.value)]
+
+
+def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
+    """One decode step: x[B, H, P], B/C[B, G, N], state[B, H, P, N] updated in place; returns y."""
+    import torch
+    bsz, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x))
+    if y is None:
+        y = torch.empty_like(x)
+    _check("ssd_decode_step", load().ssd_decode_step(
+        ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
+        _ptr(y), _stream(stream)))
+    return y

@@ -1,0 +1,325 @@
+// libssd C ABI: argument validation, aliasing rules and dispatch to the HIP
+// kernels.  The contract of every entry point is documented in include/ssd.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "ssd.h"
+#include "ssd_kernels.h"
+
+#define SSD_EXPORT extern "C" __attribute__((visibility("default")))
+
+namespace ssd {
+
+hipError_t log_begin(EventLog *log, hipStream_t s)
+{
+    if (!log || !log->on)
+        return hipSuccess;
+    log->n = 0;
+    return hipEventRecord(log->ev[0], s);
+}
+
+hipError_t log_kernel(EventLog *log, const char *name, hipStream_t s)
+{
+    if (!log || !log->on)
+        return hipSuccess;
+    if (log->n >= kMaxTimedKernels)
+        return hipErrorInvalidValue;
+    log->name[log->n] = name;
+    ++log->n;
+    return hipEventRecord(log->ev[log->n], s);
+}
+
+}  // namespace ssd
+
+namespace {
+
+constexpr int64_t kMaxHeads = 1 << 16;
+
+bool mul_ok(int64_t a, int64_t b, int64_t *out)
+{
+    return !__builtin_mul_overflow(a, b, out) && *out < (int64_t(1) << 60);
+}
+
+// Basic size checks shared by every entry point.
+ssd_status check_dims(const ssd_dims *d, bool uses_chunk)
+{
+    if (!d)
+        return SSD_ERR_NULL;
+    if (d->reserved != 0)
+        return SSD_ERR_SHAPE;
+    if (d->batch < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1)
+        return SSD_ERR_SHAPE;
+    if (uses_chunk && (d->seqlen < 0 || d->chunk < 1))
+        return SSD_ERR_SHAPE;
+    if (d->nheads % d->ngroups != 0)
+        return SSD_ERR_SHAPE;
+    if (d->io_dtype != SSD_F32 && d->io_dtype != SSD_BF16)
+        return SSD_ERR_UNSUPPORTED;
+    if (d->nheads > kMaxHeads)
+        return SSD_ERR_UNSUPPORTED;
+    int64_t t;
+    const int64_t L = uses_chunk ? (d->seqlen > 0 ? d->seqlen : 1) : 1;
+    if (!mul_ok(d->batch, L, &t) || !mul_ok(t, d->nheads, &t) || !mul_ok(t, d->headdim, &t) ||
+        !mul_ok(t, 4, &t))
+        return SSD_ERR_SHAPE;
+    if (!mul_ok(d->batch, L, &t) || !mul_ok(t, d->ngroups, &t) || !mul_ok(t, d->dstate, &t) ||
+        !mul_ok(t, 4, &t))
+        return SSD_ERR_SHAPE;
+    if (!mul_ok(d->batch, d->nheads, &t) || !mul_ok(t, d->headdim, &t) ||
+        !mul_ok(t, d->dstate, &t) || !mul_ok(t, 4, &t))
+        return SSD_ERR_SHAPE;
+    if (d->batch * d->nheads > INT32_MAX)
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+struct Span {
+    uintptr_t lo, hi;
+};
+Span span(const void *p, int64_t bytes)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return {lo, lo + (uintptr_t)(bytes > 0 ? bytes : 0)};
+}
+bool overlap(Span a, Span b)
+{
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+bool aligned(const void *p, uintptr_t n)
+{
+    return reinterpret_cast<uintptr_t>(p) % n == 0;
+}
+
+ssd_status device_status(hipError_t e)
+{
+    return e == hipSuccess ? SSD_OK : SSD_ERR_DEVICE;
+}
+
+ssd_status scan_supported(const ssd_dims *d)
+{
+    if (d->io_dtype == SSD_BF16) {
+        if (d->headdim != 64 || d->dstate != 128 || d->chunk % 64 != 0 || d->chunk > 512)
+            return SSD_ERR_UNSUPPORTED;
+    } else {
+        if (d->headdim > 64 || d->dstate > 128 || d->chunk > 256)
+            return SSD_ERR_UNSUPPORTED;
+    }
+    return SSD_OK;
+}
+
+size_t scan_workspace(const ssd_dims *d)
+{
+    if (d->io_dtype != SSD_BF16 || d->batch == 0 || d->seqlen == 0)
+        return 0;
+    return ssd::plan_scan_bf16(d->batch, d->seqlen, d->nheads, d->chunk).ws_bytes;
+}
+
+ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const float *A,
+                    const void *B, const void *C, const float *D, const float *init, void *y,
+                    float *fin, void *ws, size_t ws_bytes, hipStream_t s, ssd::EventLog *log)
+{
+    ssd_status st = check_dims(d, true);
+    if (st != SSD_OK)
+        return st;
+    if ((st = scan_supported(d)) != SSD_OK)
+        return st;
+    if (d->batch == 0)
+        return SSD_OK;
+    if (!fin)
+        return SSD_ERR_NULL;
+    const int64_t esz = d->io_dtype == SSD_BF16 ? 2 : 4;
+    const int64_t Bn = d->batch, L = d->seqlen, H = d->nheads, P = d->headdim, N = d->dstate,
+                  G = d->ngroups;
+    const int64_t state_bytes = Bn * H * P * N * 4;
+    if (!aligned(fin, 16) || (init && !aligned(init, 16)))
+        return SSD_ERR_ALIGNMENT;
+    const Span sfin = span(fin, state_bytes), sinit = span(init, state_bytes);
+    if (init && init != fin && overlap(sfin, sinit))
+        return SSD_ERR_ALIAS;
+    if (L == 0) {
+        // no tokens: the cache is handed through unchanged
+        return device_status(ssd::launch_state_init(fin, init, Bn * H * P * N, s));
+    }
+    if (!x || !dt || !A || !B || !C || !D || !y)
+        return SSD_ERR_NULL;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4))
+        return SSD_ERR_ALIGNMENT;
+    const size_t need = scan_workspace(d);
+    if (need > 0 && (!ws || ws_bytes < need))
+        return SSD_ERR_WORKSPACE;
+    if (need > 0 && !aligned(ws, 16))
+        return SSD_ERR_ALIGNMENT;
+    const Span sy = span(y, Bn * L * H * P * esz);
+    const Span sws = span(ws, (int64_t)need);
+    const Span ins[] = {span(x, Bn * L * H * P * esz), span(dt, Bn * L * H * 4), span(A, H * 4),
+                        span(B, Bn * L * G * N * esz), span(C, Bn * L * G * N * esz),
+                        span(D, H * 4), sinit, sfin, sws};
+    for (const Span &in : ins)
+        if (overlap(sy, in))
+            return SSD_ERR_ALIAS;
+    const Span ins2[] = {span(x, Bn * L * H * P * esz), span(dt, Bn * L * H * 4),
+                         span(A, H * 4), span(B, Bn * L * G * N * esz),
+                         span(C, Bn * L * G * N * esz), span(D, H * 4)};
+    for (const Span &in : ins2)
+        if (overlap(sfin, in) || overlap(sws, in))
+            return SSD_ERR_ALIAS;
+    if (overlap(sws, sfin) || overlap(sws, sinit))
+        return SSD_ERR_ALIAS;
+
+    hipError_t e;
+    if (d->io_dtype == SSD_BF16) {
+        const ssd::Bf16Plan plan = ssd::plan_scan_bf16(Bn, L, H, d->chunk);
+        e = ssd::launch_scan_bf16(plan, Bn, L, H, G, d->chunk, x, dt, A, B, C, D, init, y, fin,
+                                  ws, s, log);
+    } else {
+        e = ssd::launch_scan_f32(Bn, L, H, P, N, G, d->chunk, static_cast<const float *>(x), dt,
+                                 A, static_cast<const float *>(B),
+                                 static_cast<const float *>(C), D, init,
+                                 static_cast<float *>(y), fin, s, log);
+    }
+    return device_status(e);
+}
+
+}  // namespace
+
+SSD_EXPORT const char *ssd_status_string(ssd_status status)
+{
+    switch (status) {
+    case SSD_OK: return "SSD_OK";
+    case SSD_ERR_NULL: return "SSD_ERR_NULL: a required pointer is NULL";
+    case SSD_ERR_SHAPE: return "SSD_ERR_SHAPE: a size is out of range or nheads % ngroups != 0";
+    case SSD_ERR_UNSUPPORTED: return "SSD_ERR_UNSUPPORTED: shape/dtype combination not implemented";
+    case SSD_ERR_ALIAS: return "SSD_ERR_ALIAS: an output overlaps a buffer it must not overlap";
+    case SSD_ERR_WORKSPACE: return "SSD_ERR_WORKSPACE: workspace missing or too small";
+    case SSD_ERR_DEVICE: return "SSD_ERR_DEVICE: a HIP call or kernel launch failed";
+    case SSD_ERR_ALIGNMENT: return "SSD_ERR_ALIGNMENT: a pointer is not aligned as required";
+    }
+    return "SSD_ERR_UNKNOWN";
+}
+
+SSD_EXPORT int ssd_version(void)
+{
+    return 10000;
+}
+
+SSD_EXPORT ssd_status ssd_state_init(const ssd_dims *dims, float *state, const float *src,
+                                     void *stream)
+{
+    ssd_status st = check_dims(dims, false);
+    if (st != SSD_OK)
+        return st;
+    if (dims->batch == 0)
+        return SSD_OK;
+    if (!state)
+        return SSD_ERR_NULL;
+    if (!aligned(state, 4) || (src && !aligned(src, 4)))
+        return SSD_ERR_ALIGNMENT;
+    const int64_t n = dims->batch * dims->nheads * dims->headdim * dims->dstate;
+    if (src && src != state && overlap(span(state, n * 4), span(src, n * 4)))
+        return SSD_ERR_ALIAS;
+    return device_status(
+        ssd::launch_state_init(state, src, n, static_cast<hipStream_t>(stream)));
+}
+
+SSD_EXPORT ssd_status ssd_chunk_scan_workspace_size(const ssd_dims *dims, size_t *bytes)
+{
+    ssd_status st = check_dims(dims, true);
+    if (st != SSD_OK)
+        return st;
+    if (!bytes)
+        return SSD_ERR_NULL;
+    if ((st = scan_supported(dims)) != SSD_OK)
+        return st;
+    *bytes = scan_workspace(dims);
+    return SSD_OK;
+}
+
+SSD_EXPORT ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const float *dt,
+                                     const float *A, const void *B, const void *C,
+                                     const float *D, const float *initial_state, void *y,
+                                     float *final_state, void *workspace, size_t workspace_bytes,
+                                     void *stream)
+{
+    return run_scan(dims, x, dt, A, B, C, D, initial_state, y, final_state, workspace,
+                    workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+SSD_EXPORT ssd_status ssd_chunk_scan_timed(const ssd_dims *dims, const void *x, const float *dt,
+                                           const float *A, const void *B, const void *C,
+                                           const float *D, const float *initial_state, void *y,
+                                           float *final_state, void *workspace,
+                                           size_t workspace_bytes, void *stream,
+                                           float *kernel_ms, const char **kernel_names,
+                                           int *n_kernels)
+{
+    if (!n_kernels || !kernel_ms)
+        return SSD_ERR_NULL;
+    ssd::EventLog log;
+    int created = 0;
+    hipError_t e = hipSuccess;
+    for (; created <= ssd::kMaxTimedKernels; ++created)
+        if ((e = hipEventCreate(&log.ev[created])) != hipSuccess)
+            break;
+    ssd_status st = SSD_OK;
+    if (e != hipSuccess) {
+        st = SSD_ERR_DEVICE;
+    } else {
+        log.on = true;
+        const hipStream_t s = static_cast<hipStream_t>(stream);
+        st = run_scan(dims, x, dt, A, B, C, D, initial_state, y, final_state, workspace,
+                      workspace_bytes, s, &log);
+        if (st == SSD_OK && hipStreamSynchronize(s) != hipSuccess)
+            st = SSD_ERR_DEVICE;
+        if (st == SSD_OK) {
+            if (log.n > *n_kernels) {
+                st = SSD_ERR_NULL;
+            } else {
+                for (int i = 0; i < log.n; ++i) {
+                    float ms = 0.f;
+                    if (hipEventElapsedTime(&ms, log.ev[i], log.ev[i + 1]) != hipSuccess)
+                        st = SSD_ERR_DEVICE;
+                    kernel_ms[i] = ms;
+                    if (kernel_names)
+                        kernel_names[i] = log.name[i];
+                }
+                *n_kernels = log.n;
+            }
+        }
+    }
+    for (int i = 0; i < created; ++i)
+        hipEventDestroy(log.ev[i]);
+    return st;
+}
+
+SSD_EXPORT ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const float *dt,
+                                      const float *A, const void *B, const void *C,
+                                      const float *D, float *state, void *y, void *stream)
+{
+    ssd_status st = check_dims(dims, false);
+    if (st != SSD_OK)
+        return st;
+    const int64_t N = dims->dstate;
+    if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256)
+        return SSD_ERR_UNSUPPORTED;
+    if (dims->batch == 0)
+        return SSD_OK;
+    if (!x || !dt || !A || !B || !C || !D || !state || !y)
+        return SSD_ERR_NULL;
+    const int64_t esz = dims->io_dtype == SSD_BF16 ? 2 : 4;
+    const int64_t Bn = dims->batch, H = dims->nheads, P = dims->headdim, G = dims->ngroups;
+    if (!aligned(state, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(x, esz) ||
+        !aligned(y, esz) || !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4))
+        return SSD_ERR_ALIGNMENT;
+    const Span ss = span(state, Bn * H * P * N * 4), sy = span(y, Bn * H * P * esz);
+    const Span ins[] = {span(x, Bn * H * P * esz), span(dt, Bn * H * 4), span(A, H * 4),
+                        span(B, Bn * G * N * esz), span(C, Bn * G * N * esz), span(D, H * 4)};
+    for (const Span &in : ins)
+        if (overlap(sy, in) || overlap(ss, in))
+            return SSD_ERR_ALIAS;
+    if (overlap(sy, ss))
+        return SSD_ERR_ALIAS;
+    return device_status(ssd::launch_decode(dims->io_dtype == SSD_BF16, Bn, H, P, N, G, x, dt, A,
+                                            B, C, D, state, y, static_cast<hipStream_t>(stream)));
+}

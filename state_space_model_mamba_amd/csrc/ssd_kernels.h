@@ -1,0 +1,54 @@
+// Internal launchers of libssd (not part of the C ABI; see include/ssd.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ssd {
+
+// Up to this many HIP events bracket the kernels of one scan (timed entry point).
+constexpr int kMaxTimedKernels = 8;
+
+struct EventLog {
+    hipEvent_t ev[kMaxTimedKernels + 1];
+    const char *name[kMaxTimedKernels];
+    int n = 0;          // kernels recorded
+    bool on = false;    // record events around launches
+};
+
+// Record the start event before the first kernel and one event after each kernel.
+hipError_t log_begin(EventLog *log, hipStream_t s);
+hipError_t log_kernel(EventLog *log, const char *name, hipStream_t s);
+
+// state[i] = src ? src[i] : 0 for i < n (fill/copy kernel, graph-capturable).
+hipError_t launch_state_init(float *state, const float *src, int64_t n, hipStream_t s);
+
+// One decode step over B*H (batch row, head) pairs; io is bf16 when bf16 != 0.
+hipError_t launch_decode(int bf16, int64_t B, int64_t H, int64_t P, int64_t N, int64_t G,
+                         const void *x, const float *dt, const float *A, const void *Bm,
+                         const void *Cm, const float *D, float *state, void *y, hipStream_t s);
+
+// fp32 chunked scan (VALU), P <= 64, N <= 128, Q <= 256.
+hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
+                           int64_t Q, const float *x, const float *dt, const float *A,
+                           const float *Bm, const float *Cm, const float *D, const float *init,
+                           float *y, float *fin, hipStream_t s, EventLog *log);
+
+// bf16 MFMA chunked scan, P = 64, N = 128, Q % 64 == 0, Q <= 512.
+struct Bf16Plan {
+    int64_t nchunks;       // ceil(L / Q)
+    int64_t chunks_per_seg;
+    int64_t nseg;          // segments per (b, h)
+    int64_t nslot;         // state slots per (b, h) in the workspace (0 if nseg == 1)
+    size_t state_bytes;    // B*H*nslot*P*N*4
+    size_t ws_bytes;       // total workspace
+};
+Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t Q);
+
+hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
+                            int64_t Q, const void *x, const float *dt, const float *A,
+                            const void *Bm, const void *Cm, const float *D, const float *init,
+                            void *y, float *fin, void *ws, hipStream_t s, EventLog *log);
+
+}  // namespace ssd

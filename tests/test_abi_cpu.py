@@ -1,0 +1,130 @@
+"""The C-ABI library loads, exports every function include/ssd.h declares, and
+rejects bad arguments before touching the device (CPU only: no call here reaches
+a kernel launch)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import state_space_model_mamba_amd as ssd
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ssd.LIBRARY):
+        pytest.fail("libssd.so is not built (run __graft_entry__.build())")
+    return ssd.load()
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(ssd.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.ssd_version() == 10000
+
+
+def test_status_strings(lib):
+    for code, name in ssd.STATUS.items():
+        assert lib.ssd_status_string(code).decode().startswith(name)
+    assert lib.ssd_status_string(99).decode() == "SSD_ERR_UNKNOWN"
+
+
+def dims(**kw):
+    base = dict(batch=4, seqlen=8192, nheads=80, headdim=64, dstate=128, ngroups=1, chunk=256,
+                io_dtype=ssd.SSD_BF16)
+    base.update(kw)
+    return ssd.make_dims(**base)
+
+
+def ws_size(lib, d):
+    n = ctypes.c_size_t(0)
+    rc = lib.ssd_chunk_scan_workspace_size(ctypes.byref(d), ctypes.byref(n))
+    return rc, n.value
+
+
+def test_workspace_size_host_logic(lib):
+    rc, n = ws_size(lib, dims())
+    assert rc == 0 and n > 0
+    # the segment states are fp32 P x N per (b, h, slot): a whole multiple of 32 KiB
+    assert (n - n % 256) % (64 * 128 * 4) == 0 or n > 4 * 80 * 64 * 128 * 4
+    assert ws_size(lib, dims(seqlen=0)) == (0, 0)
+    assert ws_size(lib, dims(batch=0)) == (0, 0)
+    assert ws_size(lib, dims(io_dtype=ssd.SSD_F32, headdim=16, dstate=16, chunk=64)) == (0, 0)
+    assert ws_size(lib, dims(headdim=32))[0] == 3        # bf16 path needs P = 64, N = 128
+    assert ws_size(lib, dims(chunk=96))[0] == 3          # Q must be a multiple of 64
+    assert ws_size(lib, dims(chunk=1024))[0] == 3
+    assert ws_size(lib, dims(ngroups=3))[0] == 2         # H % G != 0
+    assert ws_size(lib, dims(nheads=0))[0] == 2
+    assert ws_size(lib, dims(seqlen=-1))[0] == 2
+    assert ws_size(lib, dims(io_dtype=7))[0] == 3
+    d = dims()
+    d.reserved = 1
+    assert ws_size(lib, d)[0] == 2
+    assert lib.ssd_chunk_scan_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == 1
+    assert lib.ssd_chunk_scan_workspace_size(ctypes.byref(dims()), None) == 1
+
+
+FAKE = 1 << 40   # a fake, well-aligned "device" address; never dereferenced here
+
+
+def scan(lib, d, x=FAKE, dt=FAKE + (1 << 33), A=FAKE + (2 << 33), B=FAKE + (3 << 33),
+         C=FAKE + (4 << 33), D=FAKE + (5 << 33), init=None, y=FAKE + (6 << 33),
+         fin=FAKE + (7 << 33), ws=FAKE + (8 << 33), ws_bytes=1 << 40):
+    p = lambda v: None if v is None else ctypes.c_void_p(v)
+    return lib.ssd_chunk_scan(ctypes.byref(d), p(x), p(dt), p(A), p(B), p(C), p(D), p(init),
+                              p(y), p(fin), p(ws), ws_bytes, None)
+
+
+def test_scan_validation(lib):
+    d = dims()
+    assert scan(lib, d, x=None) == 1
+    assert scan(lib, d, fin=None) == 1
+    assert scan(lib, d, ws=None) == 5
+    assert scan(lib, d, ws_bytes=16) == 5
+    assert scan(lib, d, y=FAKE + 64) == 4                 # y overlaps x
+    assert scan(lib, d, y=FAKE + (8 << 33) + 1024) == 4   # y overlaps the workspace
+    assert scan(lib, d, fin=FAKE + 256) == 4              # final state overlaps x
+    assert scan(lib, d, init=FAKE + (7 << 33) + 4096) == 4  # partial init/final overlap
+    assert scan(lib, d, x=FAKE + 2) == 7                  # misaligned
+    assert scan(lib, dims(headdim=48)) == 3
+    assert scan(lib, dims(ngroups=3)) == 2
+    assert scan(lib, dims(batch=0), x=None, y=None, fin=None) == 0   # empty batch: no-op
+    assert lib.ssd_chunk_scan(None, *([None] * 10), 0, None) == 1
+
+
+def test_decode_validation(lib):
+    p = ctypes.c_void_p
+    d = dims()
+    base = [p(FAKE + (k << 33)) for k in range(8)]
+
+    def call(*over, **kw):
+        args = list(base)
+        for i, v in over:
+            args[i] = v
+        return lib.ssd_decode_step(ctypes.byref(kw.get("d", d)), *args, None)
+
+    assert call((0, None)) == 1
+    assert call((7, p(FAKE + (6 << 33) + 64))) == 4     # y overlaps the state
+    assert call((6, p(FAKE + 64))) == 4                 # state overlaps x
+    assert call(d=dims(dstate=96)) == 3
+    assert call(d=dims(ngroups=7)) == 2
+    assert call((6, p(FAKE + (6 << 33) + 4))) == 7      # misaligned state
+    assert lib.ssd_decode_step(ctypes.byref(dims(batch=0)), *([None] * 8), None) == 0
+
+
+def test_state_init_validation(lib):
+    d = dims()
+    assert lib.ssd_state_init(ctypes.byref(d), None, None, None) == 1
+    assert lib.ssd_state_init(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), None) == 4
+    assert lib.ssd_state_init(ctypes.byref(dims(batch=0)), None, None, None) == 0

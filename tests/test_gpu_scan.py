@@ -1,0 +1,242 @@
+"""GPU parity of ssd_chunk_scan (and prefill -> decode continuity) against the
+fp64 oracle, on the five seeded workloads and on edge cases."""
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import ssd_inputs as si
+import state_space_model_mamba_amd as ssd
+from parity import (TOL, check_state, check_y, dev, host, oracle_heads, rel, sample_pairs,
+                    widen_inputs)
+
+pytestmark = pytest.mark.gpu
+
+
+def gpu_inputs(w, inp):
+    A, D = si.head_params(w)
+    return dict(x=dev(inp["x"], w.io), dt=dev(inp["dt"]), B=dev(inp["B"], w.io),
+                C=dev(inp["C"], w.io), A=dev(A), D=dev(D)), A, D
+
+
+def gpu_scan(g, chunk, D=None, init=None, **kw):
+    y, s = ssd.ssd_chunk_scan(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"] if D is None else D,
+                              chunk, initial_state=init, **kw)
+    torch.cuda.synchronize()
+    return y, s
+
+
+def full_check(w, Q=None, h0=None, zero_D=True):
+    """GPU scan vs the oracle over the whole input (small workloads)."""
+    Q = Q or w.chunk
+    inp = si.prefill_inputs(w)
+    g, A, D = gpu_inputs(w, inp)
+    wid = widen_inputs(inp, w.io)
+    tol = TOL[w.io]
+    init = None if h0 is None else dev(h0.astype(np.float32))
+    y, s = gpu_scan(g, Q, init=init)
+    h0d = None if h0 is None else h0.astype(np.float32).astype(np.float64)
+    yref, sref = oracle.ssd_scan(wid["x"], wid["dt"], A, wid["B"], wid["C"], D, h0=h0d, nthreads=16)
+    check_y(host(y), yref, tol)
+    check_state(host(s), sref, tol)
+    if zero_D:
+        # D masks most of y (|y - D x| is under 1% of |y|); rerun with D = 0 so the
+        # SSM part alone is held to the same tolerance.
+        y0, s0 = gpu_scan(g, Q, D=torch.zeros_like(g["D"]), init=init)
+        yref0, _ = oracle.ssd_scan(wid["x"], wid["dt"], A, wid["B"], wid["C"], np.zeros_like(D),
+                                   h0=h0d, nthreads=16)
+        check_y(host(y0), yref0, tol, "y (D = 0)")
+        assert np.array_equal(host(s0), host(s))
+    return g, A, D, y, s
+
+
+# --------------------------------------------------------------------------
+# the five workloads
+# --------------------------------------------------------------------------
+def test_tiny_f32_prefill_then_decode():
+    """256-token fp32 prefill, then 16 decode steps from its final state; all
+    272 outputs and the final state against the oracle's 272-token recurrence."""
+    w = si.WORKLOADS["tiny_f32"]
+    inp = si.prefill_inputs(w)
+    g, A, D = gpu_inputs(w, inp)
+    y, s = gpu_scan(g, w.chunk)
+    tok = si.decode_tokens(w, w.batch, 0, w.decode_steps)
+    ys = []
+    for k in range(w.decode_steps):
+        ys.append(ssd.ssd_decode_step(dev(tok["x"][k]), dev(tok["dt"][k]), g["A"], dev(tok["B"][k]),
+                                      dev(tok["C"][k]), g["D"], s))
+    torch.cuda.synchronize()
+    y_all = np.concatenate([host(y), np.stack([host(t) for t in ys], axis=1)], axis=1)
+    wid = widen_inputs(inp, "f32")
+    seq = {k: np.concatenate([wid[k], (tok[k].astype(np.float64)).transpose(1, 0, *range(2, tok[k].ndim))], axis=1)
+           for k in ("x", "dt", "B", "C")}
+    yref, sref = oracle.ssd_scan(seq["x"], seq["dt"], A, seq["B"], seq["C"], D)
+    check_y(y_all, yref, TOL["f32"], "y (prefill + decode)")
+    check_state(host(s), sref, TOL["f32"], "state after decode")
+
+
+def test_m2_130m_full():
+    full_check(si.WORKLOADS["m2_130m"])
+
+
+def test_m2_2p7b_sampled_heads():
+    """Full-size 2.7B layer (B=4, L=8192, H=80); the oracle runs 16 sampled
+    (b, h) sequences in full (each 8192 tokens), with and without D."""
+    w = si.WORKLOADS["m2_2p7b"]
+    inp = si.prefill_inputs(w)
+    g, A, D = gpu_inputs(w, inp)
+    y, s = gpu_scan(g, w.chunk)
+    y0, _ = gpu_scan(g, w.chunk, D=torch.zeros_like(g["D"]))
+    pairs = sample_pairs(w.batch, w.nheads, 16, seed=2)
+    yref, sref = oracle_heads(inp, w.io, A, D, pairs)
+    yref0, _ = oracle_heads(inp, w.io, A, np.zeros_like(D), pairs)
+    yh, y0h, sh = host(y), host(y0), host(s)
+    tol = TOL[w.io]
+    for i, (b, h) in enumerate(pairs):
+        assert rel(yh[b, :, h], yref[i]) <= tol, (b, h, rel(yh[b, :, h], yref[i]))
+        assert rel(y0h[b, :, h], yref0[i]) <= tol, (b, h, rel(y0h[b, :, h], yref0[i]))
+        assert rel(sh[b, h], sref[i]) <= tol, (b, h, rel(sh[b, h], sref[i]))
+    assert np.all(np.isfinite(yh)) and np.all(np.isfinite(sh))
+
+
+def test_longctx_prefix_fullrun_and_decode_continuity():
+    """131072 tokens, 8 groups: (1) the [0, 4096) prefix as its own scan against
+    the oracle; (2) the full-length scan on 8 sampled heads against the oracle's
+    131072-step recurrence; (3) 256 decode steps from the GPU's final state
+    against the oracle started from that same state."""
+    w = si.WORKLOADS["longctx_2p7b"]
+    A, D = si.head_params(w)
+    tol = TOL[w.io]
+    # (1) prefix
+    pre = si.prefill_inputs(w, 0, w.prefix)
+    gp, _, _ = gpu_inputs(w, pre)
+    yp, sp = gpu_scan(gp, w.chunk)
+    wp = widen_inputs(pre, w.io)
+    yref, sref = oracle.ssd_scan(wp["x"], wp["dt"], A, wp["B"], wp["C"], D, nthreads=16)
+    check_y(host(yp), yref, tol, "prefix y")
+    check_state(host(sp), sref, tol, "prefix state")
+    del gp, yp, sp, wp, yref, sref
+    # (2) full length
+    inp = si.prefill_inputs(w)
+    g, _, _ = gpu_inputs(w, inp)
+    y, s = gpu_scan(g, w.chunk)
+    pairs = [(0, h) for h in (0, 9, 10, 37, 41, 63, 70, 79)]
+    yr, sr = oracle_heads(inp, w.io, A, D, pairs)
+    yh, sh = host(y), host(s)
+    for i, (b, h) in enumerate(pairs):
+        assert rel(yh[b, :, h], yr[i]) <= tol, (h, rel(yh[b, :, h], yr[i]))
+        assert rel(sh[b, h], sr[i]) <= tol, (h, rel(sh[b, h], sr[i]))
+    del g, y, inp
+    # (3) decode continuity from the GPU's own final state
+    tok = si.decode_tokens(w, w.batch, 0, w.decode_steps)
+    dA, dD = dev(A), dev(D)
+    ys = []
+    s_run = s.clone()
+    for k in range(w.decode_steps):
+        ys.append(ssd.ssd_decode_step(dev(tok["x"][k], w.io), dev(tok["dt"][k]), dA,
+                                      dev(tok["B"][k], w.io), dev(tok["C"][k], w.io), dD, s_run))
+    torch.cuda.synchronize()
+    yd = np.stack([host(t) for t in ys], axis=1)
+    seq = {"x": si.widen(tok["x"], w.io).transpose(1, 0, 2, 3),
+           "dt": tok["dt"].astype(np.float64).transpose(1, 0, 2),
+           "B": si.widen(tok["B"], w.io).transpose(1, 0, 2, 3),
+           "C": si.widen(tok["C"], w.io).transpose(1, 0, 2, 3)}
+    ydr, sdr = oracle.ssd_scan(seq["x"], seq["dt"], A, seq["B"], seq["C"], D, h0=sh, nthreads=16)
+    check_y(yd, ydr, tol, "decode after long prefill")
+    check_state(host(s_run), sdr, tol, "state after long prefill + decode")
+
+
+# --------------------------------------------------------------------------
+# chunk length, raggedness, groups, segments
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("Q", [64, 128, 256, 512])
+def test_chunk_size_invariance(Q):
+    w = si.small_workload(batch=2, seqlen=1000, nheads=4, ngroups=2, chunk=Q, seed=21)
+    full_check(w, Q)
+
+
+@pytest.mark.parametrize("L", [1, 17, 63, 64, 65, 130, 255, 257])
+def test_ragged_lengths(L):
+    w = si.small_workload(batch=2, seqlen=L, nheads=3, ngroups=1, chunk=128, seed=L)
+    full_check(w)
+
+
+@pytest.mark.parametrize("H,G", [(8, 8), (8, 2), (10, 5)])
+def test_groups(H, G):
+    w = si.small_workload(batch=1, seqlen=700, nheads=H, ngroups=G, chunk=64, seed=H * 31 + G)
+    full_check(w)
+
+
+@pytest.mark.parametrize("target", ["1", "4096"])
+def test_segment_count_extremes(target, monkeypatch):
+    """One segment per sequence, and one segment per chunk."""
+    monkeypatch.setenv("SSD_SEG_TARGET_WG", target)
+    w = si.small_workload(batch=2, seqlen=2048 + 77, nheads=2, chunk=64, seed=5)
+    full_check(w)
+
+
+def test_initial_state_and_split_continuity():
+    """scan(L) == scan(k) then scan(L - k, initial_state = that final state), for
+    a given non-zero initial state; and final_state may alias initial_state."""
+    w = si.small_workload(batch=2, seqlen=900, nheads=4, chunk=128, seed=9)
+    h0 = np.random.default_rng(1).standard_normal((2, 4, 64, 128)).astype(np.float32)
+    g, A, D, y, s = full_check(w, h0=h0, zero_D=False)
+    inp = si.prefill_inputs(w)
+    for k in (128, 333):
+        a = {key: v[:, :k] for key, v in inp.items()}
+        b = {key: v[:, k:] for key, v in inp.items()}
+        ga, _, _ = gpu_inputs(w, a)
+        gb, _, _ = gpu_inputs(w, b)
+        state = dev(h0.copy())
+        ya, _ = gpu_scan(ga, w.chunk, init=state, final_state=state)    # in place
+        yb, _ = gpu_scan(gb, w.chunk, init=state, final_state=state)
+        yab = np.concatenate([host(ya), host(yb)], axis=1)
+        assert rel(yab, host(y)) < TOL["bf16"] and rel(host(state), host(s)) < TOL["bf16"]
+
+
+def test_empty_inputs():
+    w = si.small_workload(batch=2, seqlen=0, nheads=4, chunk=64, seed=3)
+    x = torch.empty((2, 0, 4, 64), dtype=torch.bfloat16, device="cuda")
+    dt = torch.empty((2, 0, 4), device="cuda")
+    Bm = torch.empty((2, 0, 1, 128), dtype=torch.bfloat16, device="cuda")
+    A = torch.full((4,), -1.0, device="cuda")
+    D = torch.ones(4, device="cuda")
+    h0 = torch.randn((2, 4, 64, 128), device="cuda")
+    y, s = ssd.ssd_chunk_scan(x, dt, A, Bm, Bm, D, 64, initial_state=h0)
+    y2, s2 = ssd.ssd_chunk_scan(x, dt, A, Bm, Bm, D, 64)
+    torch.cuda.synchronize()
+    assert y.numel() == 0 and torch.equal(s, h0) and torch.count_nonzero(s2) == 0
+    xb = torch.empty((0, 10, 4, 64), dtype=torch.bfloat16, device="cuda")
+    yb, sb = ssd.ssd_chunk_scan(xb, torch.empty((0, 10, 4), device="cuda"), A,
+                                torch.empty((0, 10, 1, 128), dtype=torch.bfloat16, device="cuda"),
+                                torch.empty((0, 10, 1, 128), dtype=torch.bfloat16, device="cuda"), D, 64)
+    assert yb.numel() == 0 and sb.numel() == 0
+
+
+@pytest.mark.parametrize("P,N,Q,L", [(64, 128, 256, 600), (16, 16, 64, 256), (32, 64, 100, 333),
+                                     (7, 5, 16, 50)])
+def test_f32_path_shapes(P, N, Q, L):
+    w = si.small_workload(batch=2, seqlen=L, nheads=4, headdim=P, dstate=N, ngroups=2, chunk=Q,
+                          io="f32", seed=P + N + Q)
+    full_check(w)
+
+
+def test_bitwise_deterministic():
+    w = si.small_workload(batch=2, seqlen=3000, nheads=8, chunk=256, seed=77)
+    inp = si.prefill_inputs(w)
+    g, _, _ = gpu_inputs(w, inp)
+    y1, s1 = gpu_scan(g, 256)
+    y2, s2 = gpu_scan(g, 256)
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+
+
+def test_timed_entry_point_matches():
+    w = si.small_workload(batch=2, seqlen=3000, nheads=8, chunk=256, seed=78)
+    inp = si.prefill_inputs(w)
+    g, _, _ = gpu_inputs(w, inp)
+    y1, s1 = gpu_scan(g, 256)
+    y2, s2, times = ssd.ssd_chunk_scan_timed(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 256)
+    assert torch.equal(y1, y2) and torch.equal(s1, s2)
+    assert [n for n, _ in times][-1] == "chunk_scan_kernel" and all(ms > 0 for _, ms in times)
