@@ -1,0 +1,348 @@
+"""Benchmark of the Mamba-2 SSD hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+A step is one ssd_chunk_scan over the Mamba-2-2.7B-shaped layer (batch 4,
+8192 tokens, 80 heads x 64, dstate 128, 1 group, chunk 256; bf16 x/B/C/y,
+fp32 dt/A/D/state), seeded synthetic inputs resident in HBM.  ``value`` is
+prefill tokens/s (batch x seqlen per step time).  The decode half of the
+metric (1000 in-place ssd_decode_step calls on a [256, 80, 64, 128] fp32 state,
+fresh tokens each step) is reported under ``decode``; batches 1, 16, 64 are
+reported as effective bandwidth (their state fits in the 256 MB MALL or the
+step is launch-bound).
+
+Prints ONE JSON line.  ``roofline`` is the dominant prefill kernel
+(chunk_scan_kernel): algorithmic bytes of the layer per launch / its average
+launch time measured with HIP events on the launch stream; ``decode.roofline``
+likewise for decode_kernel.  ``traffic`` comes from committed rocprofv3
+FETCH_SIZE / WRITE_SIZE counters (profiles/traffic.json) when they were taken
+on the current kernel sources, else null.  ``cpu_baseline`` times the fp64
+oracle (as it stands) on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+METRIC = "SSD prefill tokens/s (MFMA %) + decode steps/s (HBM GB/s %) at 2.7B-layer shape"
+KERNEL_SOURCES = ["state_space_model_mamba_amd/csrc/ssd_scan_bf16.hip",
+                  "state_space_model_mamba_amd/csrc/ssd_decode.hip"]
+
+
+def prefill_bytes(w) -> int:
+    """Minimum HBM bytes of one prefill: read x, B, C, dt, write y and the final state."""
+    esz = 2
+    x = w.batch * w.seqlen * w.nheads * w.headdim * esz
+    bc = 2 * w.batch * w.seqlen * w.ngroups * w.dstate * esz
+    dt = w.batch * w.seqlen * w.nheads * 4
+    state = w.batch * w.nheads * w.headdim * w.dstate * 4
+    return 2 * x + bc + dt + state + 2 * w.nheads * 4
+
+
+def prefill_useful_flops(w) -> int:
+    """Useful FLOPs of the chunked algorithm (causal triangle only): C B^T per
+    group, intra-chunk product, chunk state and state->output per head."""
+    Q, P, N = w.chunk, w.headdim, w.dstate
+    nc = w.seqlen // Q
+    tri = Q * (Q + 1) // 2
+    cb = tri * N * 2 * w.batch * nc * w.ngroups
+    per_head = (tri * P * 2 + 2 * Q * P * N * 2) * w.batch * nc * w.nheads
+    return cb + per_head
+
+
+def decode_bytes(b, w) -> int:
+    """HBM bytes of one decode step: state read + write, x, y, B, C, dt."""
+    state = b * w.nheads * w.headdim * w.dstate * 4
+    return 2 * state + 2 * b * w.nheads * w.headdim * 2 + 2 * b * w.ngroups * w.dstate * 2 + b * w.nheads * 4
+
+
+def source_digest() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()
+
+
+def committed_traffic(kernel: str):
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != source_digest():
+        return None
+    k = rec.get("kernels", {}).get(kernel)
+    if not k:
+        return None
+    return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
+            "total_bytes": k["fetch_bytes"] + k["write_bytes"], "scale": rec.get("copy_scale"),
+            "source": "profiles/traffic.json"}
+
+
+def to_dev(a, bf16=False):
+    import torch
+    if bf16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def bench_prefill(args):
+    import torch
+
+    import ssd_inputs as si
+    import state_space_model_mamba_amd as ssd
+
+    w = si.WORKLOADS["m2_2p7b"]
+    A, D = si.head_params(w)
+    inp = si.prefill_inputs(w)
+    x, dt = to_dev(inp["x"], True), to_dev(inp["dt"])
+    B, C = to_dev(inp["B"], True), to_dev(inp["C"], True)
+    dA, dD = to_dev(A), to_dev(D)
+    y = torch.empty_like(x)
+    fs = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device="cuda")
+    nws = ssd.ssd_chunk_scan_workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
+                                            w.ngroups, w.chunk)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    del inp
+
+    def step():
+        ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    ms = wall * 1e3 / args.steps
+
+    # per-kernel device times, HIP events recorded around each launch on this stream
+    per = {}
+    for _ in range(max(3, min(args.steps, 10))):
+        _, _, times = ssd.ssd_chunk_scan_timed(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs,
+                                               workspace=ws)
+        for name, t in times:
+            per.setdefault(name, []).append(t)
+    kern = {k: float(np.mean(v)) for k, v in per.items()}
+    nbytes = prefill_bytes(w)
+    flops = prefill_useful_flops(w)
+    k3 = kern["chunk_scan_kernel"]
+    tokens = w.batch * w.seqlen
+    res = {
+        "w": w, "ms": ms, "ev_ms": ev_ms, "tokens_per_s": tokens / (ms * 1e-3),
+        "kernels_ms": kern, "bytes": nbytes, "flops": flops,
+        "roofline": {
+            "bound": "hbm", "kernel": "chunk_scan_kernel",
+            "achieved": nbytes / (k3 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": nbytes / (k3 * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "traffic": committed_traffic("chunk_scan_kernel"),
+            "bytes_per_launch": nbytes, "avg_launch_ms": k3,
+        },
+        "mfma": {
+            "useful_gflop_per_step": flops / 1e9,
+            "achieved_tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "note": "useful (causal-triangle) FLOPs of the whole scan per step time; "
+                    "rocprof MFMA busy counters are in profiles/",
+        },
+        "path_gbs": nbytes / (ms * 1e-3) / 1e9,
+    }
+    return res
+
+
+def bench_decode(args):
+    import torch
+
+    import ssd_inputs as si
+    import state_space_model_mamba_amd as ssd
+
+    w = si.WORKLOADS["decode_2p7b"]
+    A, D = si.head_params(w)
+    dA, dD = to_dev(A), to_dev(D)
+    out = {}
+    for b in args.decode_batches:
+        steps = args.decode_steps
+        tok = si.decode_tokens(w, b, 0, steps)
+        x, dt = to_dev(tok["x"], True), to_dev(tok["dt"])
+        B, C = to_dev(tok["B"], True), to_dev(tok["C"], True)
+        del tok
+        state = to_dev(si.random_state(w, b))
+        y = torch.empty((steps, b, w.nheads, w.headdim), dtype=torch.bfloat16, device="cuda")
+        for k in range(min(5, steps)):             # warm-up (advances the state)
+            ssd.ssd_decode_step(x[k], dt[k], dA, B[k], C[k], dD, state, y=y[k])
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0 = time.perf_counter()
+        e0.record()
+        for k in range(steps):
+            ssd.ssd_decode_step(x[k], dt[k], dA, B[k], C[k], dD, state, y=y[k])
+        e1.record()
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        ev_ms = e0.elapsed_time(e1) / steps
+        nb = decode_bytes(b, w)
+        out[b] = {"steps": steps, "ms_per_step": wall * 1e3 / steps, "event_ms_per_step": ev_ms,
+                  "steps_per_s": steps / wall, "bytes_per_step": nb,
+                  "gbs": nb / (ev_ms * 1e-3) / 1e9, "frac": nb / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        del x, dt, B, C, y, state
+        torch.cuda.empty_cache()
+    return w, out
+
+
+def cpu_baseline_prefill(w, npairs=64):
+    """The fp64 oracle on `npairs` of the layer's (batch, head) sequences, full
+    length each, threaded over pairs; tokens/s scaled to the whole layer."""
+    import oracle
+    import ssd_inputs as si
+
+    threads = min(16, os.cpu_count() or 1)
+    A, D = si.head_params(w)
+    inp = si.prefill_inputs(w)
+    H = w.nheads
+    pairs = [(k // H, k % H) for k in range(npairs)]
+    xs = np.stack([si.widen(inp["x"][b, :, h], "bf16") for b, h in pairs])[:, :, None]
+    dts = np.stack([inp["dt"][b, :, h] for b, h in pairs]).astype(np.float64)[:, :, None]
+    Bs = np.stack([si.widen(inp["B"][b, :, 0], "bf16") for b, h in pairs])[:, :, None]
+    Cs = np.stack([si.widen(inp["C"][b, :, 0], "bf16") for b, h in pairs])[:, :, None]
+    del inp
+    from concurrent.futures import ThreadPoolExecutor
+
+    def one(i):
+        b, h = pairs[i]
+        oracle.ssd_scan(xs[i:i + 1], dts[i:i + 1], A[h:h + 1], Bs[i:i + 1], Cs[i:i + 1], D[h:h + 1])
+
+    oracle.load()
+    t0 = time.perf_counter()
+    with ThreadPoolExecutor(threads) as ex:
+        list(ex.map(one, range(npairs)))
+    T = time.perf_counter() - t0
+    full_pairs = w.batch * H
+    tok_s = (w.batch * w.seqlen) / (T * full_pairs / npairs)
+    return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"fp64 oracle on {npairs} of the {full_pairs} (batch, head) sequences of "
+                      f"the {w.batch}x{w.seqlen}x{H} layer, all {w.seqlen} tokens each, "
+                      f"{threads} threads over sequences; {T:.2f} s wall, tokens/s scaled by "
+                      f"{npairs}/{full_pairs}"}
+
+
+def cpu_baseline_decode(w, batch=256, nseq=16, steps=50):
+    """The oracle's decode step on `nseq` sequences for `steps` steps, steps/s
+    scaled to the full batch."""
+    import oracle
+    import ssd_inputs as si
+
+    threads = min(16, os.cpu_count() or 1)
+    A, D = si.head_params(w)
+    tok = si.decode_tokens(w, nseq, 0, steps)
+    st = si.random_state(w, nseq).astype(np.float64)
+    xs = si.widen(tok["x"], "bf16")
+    Bs, Cs = si.widen(tok["B"], "bf16"), si.widen(tok["C"], "bf16")
+    dts = tok["dt"].astype(np.float64)
+    t0 = time.perf_counter()
+    for k in range(steps):
+        _, st = oracle.ssd_decode_step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, nthreads=threads)
+    T = time.perf_counter() - t0
+    return {"value": steps / (T * batch / nseq), "unit": "steps/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"{nseq} of {batch} sequences x {steps} steps; scaled by {nseq}/{batch}"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--decode-batches", type=str, default="256,64,16,1")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
+    args = ap.parse_args()
+    args.decode_batches = [int(v) for v in args.decode_batches.split(",") if v]
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the SSD hot path here is a single-GPU build "
+              "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    torch.cuda.set_device(0)
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)                 # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        del src, dst
+    pre = bench_prefill(args)
+    w = pre["w"]
+    line = {
+        "metric": METRIC,
+        "value": pre["tokens_per_s"],
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Mamba-2-2.7B-shaped SSD layer prefill (ssd_chunk_scan)",
+                   "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk": w.chunk, "state": "fp32", "io": "bf16"},
+        "event_ms_per_step": pre["ev_ms"],
+        "kernels_ms": pre["kernels_ms"],
+        "path_gbs": pre["path_gbs"],
+        "roofline": pre["roofline"],
+        "mfma": pre["mfma"],
+    }
+    if not args.no_decode:
+        wd, dec = bench_decode(args)
+        main_b = max(dec)
+        d = dec[main_b]
+        line["decode"] = {
+            "workload": f"decode_step at the 2.7B shape, state [{main_b},80,64,128] fp32, "
+                        f"{d['steps']} consecutive in-place steps, fresh bf16 tokens",
+            "steps_per_s": d["steps_per_s"], "ms_per_step": d["ms_per_step"],
+            "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": d["gbs"],
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
+                         "traffic": committed_traffic("decode_kernel"),
+                         "bytes_per_launch": d["bytes_per_step"],
+                         "avg_launch_ms": d["event_ms_per_step"]},
+            "batches": {str(b): {k: v for k, v in r.items()} for b, r in sorted(dec.items())},
+            "note": "batch <= 64 keeps the state (<= 168 MB) in the 256 MB MALL or is "
+                    "launch-bound: effective bandwidth, not HBM",
+        }
+        if not args.no_cpu_baseline:
+            line["decode"]["cpu_baseline"] = cpu_baseline_decode(wd)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()
