@@ -90,6 +90,52 @@ def committed_traffic(kernel: str):
             "source": "profiles/traffic.json"}
 
 
+COPY_KERNEL = "__amd_rocclr_copyBuffer"     # the device copy made by --copy-calibration
+COPY_BYTES = 1 << 30
+
+
+def _counter_means(path, counter):
+    """Per-kernel mean of one rocprofv3 counter (KiB per dispatch) and the copy total."""
+    import csv
+    per, copy = {}, 0.0
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        name = r["Kernel_Name"]
+        v = float(r["Counter_Value"])
+        if name.startswith(COPY_KERNEL):
+            copy += v
+        short = name.split("(")[0].split("::")[-1]
+        for k in ("decay_prep_kernel", "seg_state_kernel", "seg_pass_kernel",
+                  "chunk_scan_kernel", "decode_kernel", "scan_f32_kernel"):
+            if k in short or k in name:
+                per.setdefault(k, []).append(v)
+    return {k: sum(v) / len(v) for k, v in per.items()}, copy
+
+
+def write_traffic(fetch_csv, write_csv):
+    """profiles/traffic.json from a FETCH_SIZE run and a WRITE_SIZE run of
+    `bench.py --copy-calibration`: each counter is scaled so that the 1 GiB copy
+    reads and writes 1 GiB."""
+    fetch, fcopy = _counter_means(fetch_csv, "FETCH_SIZE")
+    write, wcopy = _counter_means(write_csv, "WRITE_SIZE")
+    if fcopy <= 0 or wcopy <= 0:
+        raise SystemExit("no copy-calibration dispatches in the counter files")
+    fs, ws = COPY_BYTES / (fcopy * 1024), COPY_BYTES / (wcopy * 1024)
+    rec = {"source_sha256": source_digest(), "copy_bytes": COPY_BYTES,
+           "copy_scale": {"fetch": fs, "write": ws},
+           "kernels": {k: {"fetch_bytes": fetch[k] * 1024 * fs,
+                           "write_bytes": write.get(k, 0.0) * 1024 * ws,
+                           "fetch_kib_raw": fetch[k], "write_kib_raw": write.get(k, 0.0)}
+                       for k in fetch}}
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    os.makedirs(os.path.dirname(path), exist_ok=True)
+    with open(path, "w") as fh:
+        json.dump(rec, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(rec, indent=1))
+
+
 def to_dev(a, bf16=False):
     import torch
     if bf16:
@@ -206,7 +252,7 @@ def bench_decode(args):
     return w, out
 
 
-def cpu_baseline_prefill(w, npairs=64):
+def cpu_baseline_prefill(w, npairs=None):
     """The fp64 oracle on `npairs` of the layer's (batch, head) sequences, full
     length each, threaded over pairs; tokens/s scaled to the whole layer."""
     import oracle
@@ -216,6 +262,7 @@ def cpu_baseline_prefill(w, npairs=64):
     A, D = si.head_params(w)
     inp = si.prefill_inputs(w)
     H = w.nheads
+    npairs = npairs or w.batch * H
     pairs = [(k // H, k % H) for k in range(npairs)]
     xs = np.stack([si.widen(inp["x"][b, :, h], "bf16") for b, h in pairs])[:, :, None]
     dts = np.stack([inp["dt"][b, :, h] for b, h in pairs]).astype(np.float64)[:, :, None]
@@ -242,7 +289,7 @@ def cpu_baseline_prefill(w, npairs=64):
                       f"{npairs}/{full_pairs}"}
 
 
-def cpu_baseline_decode(w, batch=256, nseq=16, steps=50):
+def cpu_baseline_decode(w, batch=256, nseq=64, steps=200):
     """The oracle's decode step on `nseq` sequences for `steps` steps, steps/s
     scaled to the full batch."""
     import oracle
@@ -275,7 +322,13 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
+    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="host only: turn two rocprofv3 counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json and exit")
     args = ap.parse_args()
+    if args.write_traffic:
+        write_traffic(*args.write_traffic)
+        return
     args.decode_batches = [int(v) for v in args.decode_batches.split(",") if v]
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SSD hot path here is a single-GPU build "
