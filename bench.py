@@ -106,8 +106,8 @@ def _counter_means(path, counter):
         if name.startswith(COPY_KERNEL):
             copy += v
         short = name.split("(")[0].split("::")[-1]
-        for k in ("decay_prep_kernel", "seg_state_kernel", "seg_pass_kernel",
-                  "chunk_scan_kernel", "decode_kernel", "scan_f32_kernel"):
+        for k in ("seg_state_kernel", "seg_pass_kernel", "chunk_scan_kernel",
+                  "decode_kernel", "scan_f32_kernel"):
             if k in short or k in name:
                 per.setdefault(k, []).append(v)
     return {k: sum(v) / len(v) for k, v in per.items()}, copy

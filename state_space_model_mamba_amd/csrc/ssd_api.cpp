@@ -112,7 +112,7 @@ size_t scan_workspace(const ssd_dims *d)
 {
     if (d->io_dtype != SSD_BF16 || d->batch == 0 || d->seqlen == 0)
         return 0;
-    return ssd::plan_scan_bf16(d->batch, d->seqlen, d->nheads, d->chunk).ws_bytes;
+    return ssd::plan_scan_bf16(d->batch, d->seqlen, d->nheads, d->ngroups, d->chunk).ws_bytes;
 }
 
 ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const float *A,
@@ -170,7 +170,7 @@ ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const flo
 
     hipError_t e;
     if (d->io_dtype == SSD_BF16) {
-        const ssd::Bf16Plan plan = ssd::plan_scan_bf16(Bn, L, H, d->chunk);
+        const ssd::Bf16Plan plan = ssd::plan_scan_bf16(Bn, L, H, G, d->chunk);
         e = ssd::launch_scan_bf16(plan, Bn, L, H, G, d->chunk, x, dt, A, B, C, D, init, y, fin,
                                   ws, s, log);
     } else {

@@ -36,18 +36,18 @@ hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N
                            float *y, float *fin, hipStream_t s, EventLog *log);
 
 // bf16 MFMA chunked scan, P = 64, N = 128, Q % 64 == 0, Q <= 512.
-// The workspace holds the segment states, their decays and the (Lam, dt) table.
+// The workspace holds the segment states and their decays.
 struct Bf16Plan {
     int64_t nchunks;       // ceil(L / Q)
+    int64_t quads;         // work-groups per (batch row, segment): G * ceil(H / G / 4)
     int64_t chunks_per_seg;
     int64_t nseg;          // segments per (b, h)
     int64_t nslot;         // state slots per (b, h) in the workspace (0 if nseg == 1)
     size_t state_bytes;    // B*H*nslot*P*N*4
     size_t decay_bytes;    // B*H*nslot*4
-    size_t ld_bytes;       // B*H*L*8: (Lam, dt) per token, head-major
     size_t ws_bytes;       // total workspace
 };
-Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t Q);
+Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q);
 
 hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
                             int64_t Q, const void *x, const float *dt, const float *A,

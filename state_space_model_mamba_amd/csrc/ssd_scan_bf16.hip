@@ -5,47 +5,54 @@
 // diagonal per head and chunkable; inside a chunk it is a causal quadratic
 // form built from einsum-style contractions under a static lower-triangular
 // mask, across chunks a state is passed along, and the decay is exponentiated
-// in float32.  With a_t = dt_t A_h and Lam_t the inclusive sum of a over the
-// current chunk (reset to 0 at every chunk start):
+// in float32.  With a_t = dt_t A_h and Lam_t the inclusive sum of a over a
+// block of tokens:
 //
 //   segsum      Lseg[t,s] = exp(Lam_t - Lam_s) for s <= t, else 0
-//   intra-chunk Y_diag   = (C B^T o Lseg) (dt x)
-//   chunk state S_out    = exp(Lam_end) S_in + sum_s exp(Lam_end - Lam_s) dt_s x_s (outer) B_s
+//   intra-block Y_diag   = (C B^T o Lseg) (dt x)
+//   block state S_out    = exp(Lam_end) S_in + sum_s exp(Lam_end - Lam_s) dt_s x_s (outer) B_s
 //   state->out  Y_off[t] = exp(Lam_t) S_in C_t
 //   output      y = Y_diag + Y_off + D_h x
 //
-// How it maps onto the chip (the page's XLA formulation is prior art only):
+// The result does not depend on the block length, so the kernels use 64-token
+// tiles with Lam referenced to the tile start (every exponent they form is a
+// difference Lam_t - Lam_s with s <= t, hence <= 0) and use the chunk length Q
+// only to place segment boundaries.  How it maps onto the chip (the page's
+// XLA formulation is prior art only):
 //
-// * A chunk is processed as 64-token tiles.  The quadratic form is evaluated
-//   on the diagonal 64 x 64 tiles only; an off-diagonal tile (s in an earlier
-//   tile of the same chunk) factorises as exp(Lam_t - Lam_e) exp(Lam_e - Lam_s)
-//   with e the last token before t's tile, so its contribution is C_t times a
-//   running state R that already holds exp(Lam_e) S_in plus the in-chunk
-//   terms.  Every exponent is <= 0, so nothing can overflow.  Per tile:
-//       Yt^T = (dt x)^T (C B^T o Lseg)^T + exp(Lam_t - Lam_e) R C^T    (MFMA)
-//       R    = exp(Lam_tile_end - Lam_e) R + (B o w)^T (dt x),         (MFMA)
-//       w_s  = exp(Lam_tile_end - Lam_s)
-// * The contractions over tokens need (dt x) and B with s running along the
-//   MFMA K lanes, but both arrive token-major.  They are staged token-major in
-//   LDS and read K-major with gfx950's transpose read (ds_read_b64_tr_b16);
-//   the per-token scale dt_s w_s of the state update is applied once while
-//   staging a second, scaled bf16 copy of the x tile, and dt_s of the
-//   diagonal block is applied to the masked C B^T tile.  That tile is produced
-//   by an MFMA in the layout the next MFMA consumes, so it never touches LDS.
+// * Two waves own one head, each half of its P rows.  A wave's 32 x 128 fp32
+//   slice of the state R lives in MFMA accumulators for the whole segment,
+//   laid out so that the state->output contraction takes its operand straight
+//   from those registers, and every product of a tile is local to the P half
+//   (y rows and state rows are both indexed by p).  Per tile:
+//       Y^T  = exp(Lam_t) R C^T + (x)^T (C B^T o Lseg o dt)^T          (MFMA)
+//       R    = exp(Lam_end) R + (B)^T (w o dt o x),  w_s = exp(Lam_end - Lam_s)
+//   with D_h folded into the diagonal of the masked C B^T tile.
+// * A work-group is four heads of one B/C group (eight waves, two per SIMD):
+//   the B and C tiles are staged once in LDS and shared, x of a head is
+//   staged by its two waves; all of it double-buffered, one barrier per tile.
+//   Each wave scans dt A of its head over the 64 tokens (lane = token), so Lam
+//   is one wave-wide prefix sum and the decay tables are private to the wave.
+// * K-major operands (B^T and x^T over tokens) come from the token-major LDS
+//   tiles through gfx950's transpose read (ds_read_b64_tr_b16); the masked
+//   C B^T tile is produced by an MFMA in the layout the next MFMA consumes.
 // * The next tile's global loads are issued before the current tile is
-//   computed and land in registers (software pipelining); they are written to
-//   LDS after the tile's closing barrier.
+//   computed and land in registers (software pipelining).
 // * Sequence parallelism: a (b, h) sequence is cut into segments of whole
-//   chunks.  Kernel 1 computes each segment's end state from a zero start
-//   (contractions for R only), kernel 2 chains the segment states
-//   (S_in[k+1] = decay_k S_in[k] + S_loc[k]), kernel 3 re-walks every segment
-//   from its true entering state and writes y (and the final state).  The
-//   last segment is never needed by kernel 1.
-// * Work-groups are remapped so that all heads of one (batch row, segment)
-//   run on the same XCD and share its L2 for the B/C tiles.
+//   chunks.  Kernel 1 computes each segment's end state from a zero start,
+//   kernel 2 chains the segment states (S_in[k+1] = decay_k S_in[k] +
+//   S_loc[k]), kernel 3 re-walks every segment from its true entering state
+//   and writes y (and the final state).  The segment count is chosen so that
+//   kernel 3 fills the chip in as few rounds as possible while every extra
+//   segment costs one more pass of its x through HBM.
+// * Work-groups are remapped so that neighbouring (batch row, segment, head
+//   quad) work lands on one XCD and shares its L2 for the B/C tiles.
 //
-// MFMA operand conventions (16x16 tiles, wave64): lane l = c + 16 g holds
-// row/column c of A/B and K-group g; the fp32 result holds D[4g + i][c].
+// MFMA operand conventions (v_mfma_f32_16x16x32_bf16, wave64): lane l = c + 16 g
+// holds row c of A / column c of B and the K-slots 8 g .. 8 g + 7; the fp32
+// result holds D[4 g + i][c].  The K index of a contraction may be assigned to
+// slots in any order as long as both operands agree; the maps used here are
+// stated where the operands are built.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -63,36 +70,39 @@ typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kP = 64, kN = 128, kT = 64;     // headdim, dstate, tile tokens
-constexpr int kThreads = 256;                 // 4 waves
-// Padded LDS row pitches (bytes): a 32-byte pad spreads the 16 rows one
-// transpose read touches over all banks.
-constexpr int kBRow = kN * 2 + 32;            // B tile [s][n]
-constexpr int kXRow = kP * 2 + 32;            // x tiles [s][p]
-constexpr int kSRow = kN * 2 + 16;            // bf16 copy of the state [p][n]
+constexpr int kHeads = 4;                     // heads per work-group
+constexpr int kWaves = 2 * kHeads;            // two waves (P halves) per head
+constexpr int kThreads = 64 * kWaves;
+// LDS row pitches (bytes).  x is read only by transpose reads: a 32-byte pad
+// spreads the rows one read touches over all banks.  C is read only row-major
+// (8 bytes at n = 32 kk + 4 g per lane, rows 16 tb + c): a 16-byte pad does it.
+// B is read both ways, which no single pitch serves, so its rows are unpadded
+// and their 16-byte chunks are permuted by an XOR with bswz(row), which makes
+// both read patterns conflict-free.
+constexpr int kBRow = kN * 2;                 // B tile [s][n], swizzled
+constexpr int kCRow = kN * 2 + 16;            // C tile [t][n]
+constexpr int kXRow = kP * 2 + 32;            // x tile [s][p]
+constexpr float kLog2e = 1.4426950408889634f;
 
-// LDS of one work-group.  The state-only kernel needs only the B tile, the
-// scaled x tile and the tile decay.
-template <bool kOut> struct TileSmem;
-template <> struct __align__(16) TileSmem<true> {
-    unsigned char Bt[kT * kBRow];   // B[s][n] of the tile
-    unsigned char Xt[kT * kXRow];   // x[s][p] of the tile (raw)
-    unsigned char Xw[kT * kXRow];   // bf16(dt_s w_s x[s][p]), w_s = exp(Lam_tile_end - Lam_s)
-    unsigned char Sb[kP * kSRow];   // bf16(R)[p][n]
-    float lam[kT];                  // chunk-referenced Lam of each token
-    float dtv[kT];                  // dt of each token (0 past the end)
-    float ed[kT];                   // exp(Lam_q - Lam_s) dt_s, q = last token of s's 16-row block
-    float scal[4];                  // [0] Lam_e (before tile), [1] tile decay
+template <bool kOut> struct ScanSmem;
+template <> struct __align__(16) ScanSmem<true> {
+    unsigned char Bt[2][kT * kBRow];          // B[s][n], ring of two tiles
+    unsigned char Ct[2][kT * kCRow];          // C[t][n]
+    unsigned char Xt[2][kHeads][kT * kXRow];  // x[s][p] of each head
+    float lam[kWaves][kT];                    // log2(e) Lam_s, tile-referenced
+    float dtv[kWaves][kT];                    // dt_s (0 past the end)
+    float vt[kWaves][kT];                     // exp(Lam_q - Lam_s) dt_s, q = last token of s's 16-block
+    float wd[kWaves][kT];                     // dt_s 2^(bias - log2(e) Lam_s), see stage_tile
 };
-template <> struct __align__(16) TileSmem<false> {
-    unsigned char Bt[kT * kBRow];
-    unsigned char Xw[kT * kXRow];
-    float scal[4];
+template <> struct __align__(16) ScanSmem<false> {
+    unsigned char Bt[2][kT * kBRow];
+    unsigned char Xt[2][kHeads][kT * kXRow];
+    float wd[kWaves][kT];
 };
 
 struct SegArgs {
     const __bf16 *x;
     const float *dt;
-    const float2 *ld;    // [B*H][L]: (Lam_t chunk-referenced, dt_t), from decay_prep_kernel
     const float *A;
     const __bf16 *B;
     const __bf16 *C;
@@ -103,8 +113,10 @@ struct SegArgs {
     float *ws_state;     // [B*H][nslot][P][N]
     float *ws_decay;     // [B*H][nslot]
     int64_t L;
-    int H, G, Q;
-    int cps;             // chunks per segment
+    int H, G;
+    int hg;              // heads per group
+    int nq;              // work-groups (head quads) per group
+    int64_t seg_tokens;  // tokens per segment (whole chunks)
     int nseg;            // segments per (b, h)
     int nseg_launch;     // segments this launch covers
     int nslot;
@@ -114,6 +126,11 @@ struct SegArgs {
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float v)
+{
+    return __builtin_amdgcn_exp2f(v);
 }
 
 // Hardware places work-group i on XCD i % 8; give each XCD a contiguous range
@@ -138,8 +155,7 @@ __device__ __forceinline__ void lds_barrier()
 
 // Inclusive prefix sum across the 64 lanes of a wave: Hillis-Steele inside
 // each 16-lane row with DPP row shifts (bound_ctrl: lanes with no source add
-// 0), then the three lower rows' totals are added with readlane.  A few cycles
-// per step, against ~100 for a shuffle through the LDS crossbar.
+// 0), then the three lower rows' totals are added with readlane.
 template <int kCtrl>
 __device__ __forceinline__ float dpp_row_shr(float v)
 {
@@ -166,9 +182,8 @@ __device__ __forceinline__ float wave_inclusive_sum(float v, int lane)
 // output lane i, element e, the element (i % 4) of the 8 bytes input lane
 // 4e + i/4 addressed.  Input lane (c, g) therefore addresses row
 // 32 j + 16 h + 4 g + c/4 and columns col0 + 4 (c % 4) .. +3, so that output
-// lane (c, g) receives column col0 + c at rows s = 32 j + 16 h + 4 g + e
-// (elements 4 h + e of the 8-element operand): the same token-to-K-slot map
-// as the C B^T tiles produced by the MFMA of the causal block.
+// lane (c, g) receives column col0 + c at rows s = 32 j + 16 h + 4 g + e in
+// K-slot 4 h + e -- the token-to-slot map of every contraction over tokens.
 __device__ __forceinline__ bf16x8 tr_operand(const unsigned char *tile, int pitch, int j,
                                              int col0, int g, int c)
 {
@@ -178,187 +193,241 @@ __device__ __forceinline__ bf16x8 tr_operand(const unsigned char *tile, int pitc
     return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// Per-work-group view of the inputs: pointers at token 0 of this (b, h) and
-// per-lane element offsets that are the same for every tile.
-struct WgIo {
-    const __bf16 *x, *B, *C;
-    const float2 *ld;                     // (Lam, dt) of this (b, h), token-contiguous
-    __bf16 *y;
-    int64_t xstride, bstride;             // elements per token
-    int offB[4], offX[2], offC;
+__device__ __forceinline__ int bswz(int row)
+{
+    return ((row & 7) << 1) | ((row >> 3) & 1);
+}
+// Byte offset of element n of row `row` in the swizzled B tile.
+__device__ __forceinline__ int boff(int row, int n)
+{
+    return row * kBRow + (((n >> 3) ^ bswz(row)) << 4) + (n & 7) * 2;
+}
+
+// tr_operand on the swizzled B tile (the row's swizzle repeats every 16 rows,
+// so the upper half of the operand sits 16 rows further down unchanged).
+__device__ __forceinline__ bf16x8 tr_operand_b(const unsigned char *tile, int j, int col0, int g,
+                                               int c)
+{
+    const unsigned char *p = tile + boff(32 * j + 4 * g + (c >> 2), col0 + 4 * (c & 3));
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * kBRow));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// n_operand on the swizzled B tile.
+__device__ __forceinline__ bf16x8 n_operand_b(const unsigned char *tile, int row, int kk, int g)
+{
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(tile + boff(row, 32 * kk + 4 * g));
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(tile + boff(row, 32 * kk + 16 + 4 * g));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// Row-major MFMA operand over n from a [row][n] LDS tile.  K-slot 4 h + i of
+// lane group g is n = 32 kk + 16 h + 4 g + i -- the map under which the state
+// accumulators (rows n = 16 nb + 4 g + i) are directly an operand.
+__device__ __forceinline__ bf16x8 n_operand(const unsigned char *tile, int pitch, int row, int kk,
+                                            int g)
+{
+    const unsigned char *p = tile + row * pitch + (32 * kk + 4 * g) * 2;
+    const bf16x4 lo = *reinterpret_cast<const bf16x4 *>(p);
+    const bf16x4 hi = *reinterpret_cast<const bf16x4 *>(p + 32);
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+// One tile's global inputs, held in registers while the previous tile is being
+// computed.  B and C are loaded by the whole work-group (16-byte chunk
+// tid + 512 r of the [64][16 x 16 B] tile); x by the two waves of its head
+// (chunk pt + 128 r of the [64][8 x 16 B] tile, pt = thread within the pair);
+// dt by every wave, lane = token.
+template <bool kOut> struct Prefetch {
+    uint4 b[2];
+    uint4 c[kOut ? 2 : 1];
+    uint4 x[4];
+    float dt;
 };
 
-// One 64-token tile's global inputs, held in registers while the previous tile
-// is being computed (software pipelining across tiles).
-struct TileRegs {
-    uint4 b[4];      // B rows: chunks tid + 256 r of the [64][16 x 16 B] tile
-    uint4 x[2];      // x rows: chunks tid + 256 r of the [64][8 x 16 B] tile
-    bf16x8 c[4];     // C row 16 w + c, n = 32 ks + 8 g .. +8 (MFMA operand layout)
-    float2 ld;       // (Lam, dt) of token t0 + lane
+struct WaveIo {
+    const __bf16 *x, *B, *C;   // at token 0 of this (b, head) / (b, group)
+    const float *dt;
+    int64_t xstride, bstride;  // elements per token
+    int dtstride;
 };
 
 // Issue the global loads of the tile starting at t0.  Always the same
-// instructions with no branches (rows past the end are clamped to the last
-// valid token and zeroed later, in store_tile), so the compiler's wait-count
-// analysis sees exactly which loads are outstanding and lets a prefetched tile
-// stay in flight while earlier tiles are consumed.  t0 itself may lie past the
-// end of the segment: the caller then simply never stores that tile.
+// instructions with no branches around them (rows past the end are clamped
+// to the last valid token and zeroed in stage_tile), so the compiler's
+// wait-count analysis sees exactly which loads are outstanding and a
+// prefetched tile stays in flight while the current one is computed.  t0 may
+// lie past the end of the segment: the caller then never stages that tile.
+// Offsets are 32-bit (a tile spans at most 64 rows of H*P or G*N elements).
 template <bool kOut>
-__device__ __forceinline__ void load_tile(TileRegs &tr, const WgIo &io, int64_t t0, int64_t L,
-                                          int tid)
+__device__ __forceinline__ void load_tile(Prefetch<kOut> &pf, const WaveIo &io, int64_t t0,
+                                          int64_t L, int tid)
 {
-    const int w = tid >> 6, l = tid & 63, c = l & 15, g = l >> 4;
-    t0 = (t0 < L) ? t0 : (L - 1) & ~(int64_t)(kT - 1);
-    const int rem = (int)((L - t0 < kT) ? (L - t0) : kT);   // valid tokens, 1 .. 64
+    const int l = tid & 63, pt = tid & 127;
+    t0 = (t0 < L) ? t0 : ((L - 1) / kT) * kT;
+    const int last = (int)((L - t0 < kT) ? (L - t0) : kT) - 1;   // last valid row
     const __bf16 *Bp = io.B + t0 * io.bstride;
-    const __bf16 *xp = io.x + t0 * io.xstride;
     const __bf16 *Cp = io.C + t0 * io.bstride;
-    const float2 *lp = io.ld + t0;
-    int oB[4], oX[2], oC = io.offC, oD = l;
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        oB[r] = io.offB[r];
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-        oX[r] = io.offX[r];
-    if (rem < kT) {                           // ragged tile: clamp rows (no loads here)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int ci = tid + kThreads * r, row = ci >> 4;
-            oB[r] = ((row < rem) ? row : rem - 1) * (int)io.bstride + (ci & 15) * 8;
-        }
-#pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const int ci = tid + kThreads * r, row = ci >> 3;
-            oX[r] = ((row < rem) ? row : rem - 1) * (int)io.xstride + (ci & 7) * 8;
-        }
-        const int rc = 16 * w + c;
-        oC = ((rc < rem) ? rc : rem - 1) * (int)io.bstride + 8 * g;
-        oD = (l < rem) ? l : rem - 1;
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r)
-        tr.b[r] = *reinterpret_cast<const uint4 *>(Bp + oB[r]);
-#pragma unroll
-    for (int r = 0; r < 2; ++r)
-        tr.x[r] = *reinterpret_cast<const uint4 *>(xp + oX[r]);
-    if constexpr (kOut) {
-#pragma unroll
-        for (int ks = 0; ks < 4; ++ks)
-            tr.c[ks] = *reinterpret_cast<const bf16x8 *>(Cp + oC + 32 * ks);
-    }
-    tr.ld = lp[oD];
-}
-
-// Registers -> LDS for one tile.  Every wave scans a_t = dt_t A_h over the 64
-// tokens (lane = token) to get the chunk-referenced Lam and w_s; wave 0 also
-// publishes the per-token tables.  lamE (Lam before the tile) is carried in
-// every wave and restarts at 0 at a chunk boundary.
-template <bool kOut>
-__device__ __forceinline__ void store_tile(TileSmem<kOut> &sm, TileRegs &tr, int64_t t0, int64_t L,
-                                           int Q, float &lamE, int tid)
-{
-    const int w = tid >> 6, l = tid & 63;
-    if (t0 % Q == 0)
-        lamE = 0.f;
-    const int rem = (int)((L - t0 < kT) ? (L - t0) : kT);
-    if (rem < kT) {                           // ragged tile: zero the clamped rows
-        const uint4 z = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            if (((tid + kThreads * r) >> 4) >= rem)
-                tr.b[r] = z;
-#pragma unroll
-        for (int r = 0; r < 2; ++r)
-            if (((tid + kThreads * r) >> 3) >= rem)
-                tr.x[r] = z;
-        if constexpr (kOut) {
-            if (16 * w + (l & 15) >= rem) {
-#pragma unroll
-                for (int ks = 0; ks < 4; ++ks)
-                    tr.c[ks] = bf16x8{};
-            }
-        }
-        if (l >= rem)
-            tr.ld.y = 0.f;                    // clamped lanes repeat the last token's Lam
-    }
-    const float lam = tr.ld.x, dtl = tr.ld.y;
-    const float lam_end = lane_f(lam, 63);
-    const float fx = dtl * __expf(lam_end - lam);     // dt_s w_s of token l
-    if (w == 0) {
-        if constexpr (kOut) {
-            const float lam_q = __shfl(lam, l | 15, 64);
-            sm.lam[l] = lam;
-            sm.dtv[l] = dtl;
-            sm.ed[l] = __expf(lam_q - lam) * dtl;
-        }
-        if (l == 0) {
-            sm.scal[0] = lamE;
-            sm.scal[1] = __expf(lam_end - lamE);
-        }
-    }
-    lamE = lam_end;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int ci = tid + kThreads * r, row = ci >> 4, col = ci & 15;
-        *reinterpret_cast<uint4 *>(sm.Bt + row * kBRow + col * 16) = tr.b[r];
-    }
+    const __bf16 *xp = io.x + t0 * io.xstride;
+    const int bs = (int)io.bstride, xs = (int)io.xstride;
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
-        const int ci = tid + kThreads * r, row = ci >> 3, col = ci & 7;
-        const float f = __shfl(fx, row, 64);
-        const bf16x8 xv = __builtin_bit_cast(bf16x8, tr.x[r]);
-        bf16x8 xs;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            xs[e] = (__bf16)((float)xv[e] * f);
-        *reinterpret_cast<bf16x8 *>(sm.Xw + row * kXRow + col * 16) = xs;
+        const int off = std::min((tid >> 4) + 32 * r, last) * bs + (tid & 15) * 8;
+        pf.b[r] = *reinterpret_cast<const uint4 *>(Bp + off);
         if constexpr (kOut)
-            *reinterpret_cast<uint4 *>(sm.Xt + row * kXRow + col * 16) = tr.x[r];
+            pf.c[r] = *reinterpret_cast<const uint4 *>(Cp + off);
     }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int off = std::min((pt >> 3) + 16 * r, last) * xs + (pt & 7) * 8;
+        pf.x[r] = *reinterpret_cast<const uint4 *>(xp + off);
+    }
+    pf.dt = io.dt[t0 * io.dtstride + std::min(l, last) * io.dtstride];
+}
+
+__device__ __forceinline__ uint4 masked(uint4 v, unsigned m)
+{
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// The state is held scaled: R = 2^ls Z with a wave-uniform ls in [-kRenorm, 0].
+// A tile's decay 2^lam_end then only moves ls (and the per-token weights of
+// the update absorb 2^-ls), instead of multiplying all of Z; Z is rescaled
+// only when ls would fall below -kRenorm, and a tile whose own decay exceeds
+// that is applied to Z directly.  Every factor formed stays within 2^(2 kRenorm).
+constexpr float kRenorm = 48.f;
+
+// Keeps the instruction scheduler from moving work across this point, so that
+// the registers of one phase of a tile are not held live through another.
+__device__ __forceinline__ void sched_fence()
+{
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// A wave-uniform condition as a scalar branch (the values it derives from are
+// wave-uniform, but the compiler cannot always prove it through the loop).
+__device__ __forceinline__ bool uniform(bool v)
+{
+    return __builtin_amdgcn_readfirstlane((int)v) != 0;
+}
+
+struct TileMode {
+    float ly;       // ls of the state entering the tile (decay of Y_off)
+    float zscale;   // direct mode: Z <- zscale Z + update
+    bool direct;
+    bool renorm;    // before the tile: Z <- rscale Z
+    float rscale;
+};
+
+// Registers -> LDS for one tile, and the tile's decay tables: each wave scans
+// a_t = dt_t A_h over its 64 tokens (lane = token), in log2 units.  Updates ls
+// (and lsum, the segment's total log2 decay) and returns how the tile treats
+// the state.
+template <bool kOut>
+__device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut> &sm, Prefetch<kOut> &pf, int slot,
+                                               int64_t t0, int64_t L, float Ah2, float &ls,
+                                               float &lsum, int tid)
+{
+    const int w = tid >> 6, l = tid & 63, pt = tid & 127;
+    const int rem = (int)((L - t0 < kT) ? (L - t0) : kT);
+    // Rows past the end are zeroed with an integer mask (a conditional choice
+    // between two uint4 aggregates would be lowered to a choice of addresses
+    // and keep the prefetch registers from being promoted out of memory).
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+        const int row = (tid >> 4) + 32 * r, col = tid & 15;
+        const unsigned m = row < rem ? ~0u : 0u;
+        *reinterpret_cast<uint4 *>(sm.Bt[slot] + row * kBRow + ((col ^ bswz(row)) << 4)) =
+            masked(pf.b[r], m);
+        if constexpr (kOut)
+            *reinterpret_cast<uint4 *>(sm.Ct[slot] + row * kCRow + col * 16) = masked(pf.c[r], m);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = (pt >> 3) + 16 * r;
+        const unsigned m = row < rem ? ~0u : 0u;
+        *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow + (pt & 7) * 16) =
+            masked(pf.x[r], m);
+    }
+    const float dtl = l < rem ? pf.dt : 0.f;
+    const float lam = wave_inclusive_sum(dtl * Ah2, l);
+    const float lam_end = lane_f(lam, 63);
+    lsum += lam_end;
+    TileMode md;
+    md.renorm = false;
+    md.rscale = 1.f;
+    float bias;                                   // wd_s = dt_s 2^(bias - lam_s)
+    if (lam_end < -kRenorm) {
+        md.direct = true;
+        md.ly = ls;
+        md.zscale = fast_exp2(ls + lam_end);
+        bias = lam_end;
+        ls = 0.f;
+    } else {
+        if (ls + lam_end < -kRenorm) {
+            md.renorm = true;
+            md.rscale = fast_exp2(ls);
+            ls = 0.f;
+        }
+        md.direct = false;
+        md.ly = ls;
+        md.zscale = 1.f;
+        bias = -ls;
+        ls += lam_end;
+    }
+    sm.wd[w][l] = fast_exp2(bias - lam) * dtl;
+    if constexpr (kOut) {
+        const float q0 = lane_f(lam, 15), q1 = lane_f(lam, 31), q2 = lane_f(lam, 47);
+        const int row = l >> 4;
+        const float lq = row == 0 ? q0 : row == 1 ? q1 : row == 2 ? q2 : lam_end;
+        sm.lam[w][l] = lam;
+        sm.dtv[w][l] = dtl;
+        sm.vt[w][l] = fast_exp2(lq - lam) * dtl;
+    }
+    return md;
 }
 
 // kOut = false: kernel 1 (segment end state from zero, written to the workspace).
 // kOut = true : kernel 3 (y and, for the last segment, the final state).
 template <bool kOut>
-__device__ __forceinline__ void seg_body(const SegArgs &a, TileSmem<kOut> &sm)
+__device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
 {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    const int hs = w >> 1;                                // head slot in the work-group
+    const int ph = w & 1;                                 // P half: p = 32 ph .. 32 ph + 31
     const int64_t j = xcd_remap(blockIdx.x, gridDim.x);
-    const int h = (int)(j % a.H);
-    const int64_t r = j / a.H;
+    const int nquad = a.G * a.nq;
+    const int quad = (int)(j % nquad);
+    const int64_t r = j / nquad;
     const int seg = (int)(r % a.nseg_launch);
     const int64_t b = r / a.nseg_launch;
-    const int grp = h / (a.H / a.G);
+    const int grp = quad / a.nq;
+    const int hw = (quad % a.nq) * kHeads + hs;           // head within the group
+    const bool active = hw < a.hg;                        // idle slots mirror the last head
+    const int h = grp * a.hg + (active ? hw : a.hg - 1);
     const int64_t bh = b * a.H + h;
     const int64_t L = a.L;
-    const int64_t tseg0 = (int64_t)seg * a.cps * a.Q;
-    const int64_t tseg1 = std::min<int64_t>(L, tseg0 + (int64_t)a.cps * a.Q);
+    const int64_t tseg0 = (int64_t)seg * a.seg_tokens;
+    const int64_t tseg1 = std::min<int64_t>(L, tseg0 + a.seg_tokens);
+    const float Ah2 = a.A[h] * kLog2e;
     const float Dh = kOut ? a.D[h] : 0.f;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
-    WgIo io;
+    WaveIo io;
     io.xstride = (int64_t)a.H * kP;
     io.bstride = (int64_t)a.G * kN;
+    io.dtstride = a.H;
     io.x = a.x + (b * L * a.H + h) * kP;
     io.B = a.B + (b * L * a.G + grp) * kN;
     io.C = a.C + (b * L * a.G + grp) * kN;
-    io.ld = a.ld + bh * L;
-    io.y = kOut ? a.y + (b * L * a.H + h) * kP : nullptr;
-#pragma unroll
-    for (int rr = 0; rr < 4; ++rr) {
-        const int ci = tid + kThreads * rr;
-        io.offB[rr] = (ci >> 4) * (int)io.bstride + (ci & 15) * 8;
-    }
-#pragma unroll
-    for (int rr = 0; rr < 2; ++rr) {
-        const int ci = tid + kThreads * rr;
-        io.offX[rr] = (ci >> 3) * (int)io.xstride + (ci & 7) * 8;
-    }
-    io.offC = (16 * w + c) * (int)io.bstride + 8 * g;
+    io.dt = a.dt + b * L * a.H + h;
+    // y of lane (c, g) in token block tb: row 16 tb + c, columns 16 (2 ph + q) + 4 g .. +3
+    const int64_t ystride = (int64_t)a.H * kP;
+    __bf16 *ybase = kOut ? a.y + (b * L * a.H + h) * kP + 32 * ph + 4 * g : nullptr;
 
-    // Running state R, held transposed: R[ni][pi][i] = R[p = 16 pi + c][n = 32 w + 16 ni + 4 g + i].
-    f32x4 R[2][4];
+    // State accumulators: Z[nb][q][i] = R[p = 32 ph + 16 q + c][n = 16 nb + 4 g + i] / 2^ls.
+    f32x4 Z[8][2];
     {
         const float *src = nullptr;
         if (kOut) {
@@ -370,281 +439,242 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, TileSmem<kOut> &sm)
                 src = a.init + bh * kP * kN;
         }
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi) {
-                R[ni][pi] = zero4;
-                if (src)
-                    R[ni][pi] = *reinterpret_cast<const f32x4 *>(
-                        src + (16 * pi + c) * kN + 32 * w + 16 * ni + 4 * g);
-            }
+            for (int q = 0; q < 2; ++q)
+                Z[nb][q] = src ? *reinterpret_cast<const f32x4 *>(
+                                     src + (32 * ph + 16 * q + c) * kN + 16 * nb + 4 * g)
+                               : zero4;
     }
-    if constexpr (kOut) {
-#pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-            for (int pi = 0; pi < 4; ++pi) {
-                bf16x4 v;
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    v[i] = (__bf16)R[ni][pi][i];
-                *reinterpret_cast<bf16x4 *>(sm.Sb + (16 * pi + c) * kSRow +
-                                            (32 * w + 16 * ni + 4 * g) * 2) = v;
-            }
-    }
+    float ls = 0.f;         // R = 2^ls Z
+    float lsum = 0.f;       // log2 of the product of tile decays over the segment
 
-    float lamE = 0.f;       // Lam at the end of the previous tile (every wave)
-    float decprod = 1.f;    // product of tile decays over the segment
-
-    // One tile: the state update always; for kOut also y of the tile, returned
-    // in yout (bf16, lane (c, g): token 16 w + c, p = 16 pi + 4 g .. +4) and
-    // stored by the caller later, so that the stores do not sit between the
-    // next tile's loads and their first use (one vmcnt counter on gfx9).
-    auto compute_tile = [&](const bf16x8 (&cop)[4], bf16x4 (&yout)[4]) {
-        // R <- exp(Lam_tile_end - Lam_e) R + B^T (dt w x): A = B^T (n rows), B = (dt w x) (p cols)
-        const float dtile = sm.scal[1];
-        decprod *= dtile;
+    // R <- zscale R + B^T (w dt x):  A = B^T (rows n), B = scaled x (columns p)
+    auto update_state = [&](const unsigned char *Bs, const bf16x8 (&XT)[2][2], const TileMode &md) {
+        f32x4 wv[2][2];
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
-            const bf16x8 bo0 = tr_operand(sm.Bt, kBRow, 0, 32 * w + 16 * ni, g, c);
-            const bf16x8 bo1 = tr_operand(sm.Bt, kBRow, 1, 32 * w + 16 * ni, g, c);
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi) {
-                const bf16x8 xo0 = tr_operand(sm.Xw, kXRow, 0, 16 * pi, g, c);
-                const bf16x8 xo1 = tr_operand(sm.Xw, kXRow, 1, 16 * pi, g, c);
-                f32x4 acc = R[ni][pi] * dtile;
-                acc = mfma32(bo0, xo0, acc);
-                acc = mfma32(bo1, xo1, acc);
-                R[ni][pi] = acc;
-            }
+            for (int hh = 0; hh < 2; ++hh)
+                wv[jj][hh] = *reinterpret_cast<const f32x4 *>(&sm.wd[w][32 * jj + 16 * hh + 4 * g]);
+        bf16x8 XS[2][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int e = 0; e < 8; ++e)
+                    XS[q][jj][e] = (__bf16)((float)XT[q][jj][e] * wv[jj][e >> 2][e & 3]);
+        if (uniform(md.direct)) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    Z[nb][q] *= md.zscale;
         }
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            const bf16x8 b0 = tr_operand_b(Bs, 0, 16 * nb, g, c);
+            const bf16x8 b1 = tr_operand_b(Bs, 1, 16 * nb, g, c);
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                Z[nb][q] = mfma32(b1, XS[q][1], mfma32(b0, XS[q][0], Z[nb][q]));
+        }
+    };
+
+    // y of the tile at t0 from the state entering it, then the state update.
+    Prefetch<kOut> pf;
+    auto compute_tile = [&](int slot, const TileMode &md, int64_t t0) {
+        const unsigned char *Xs = sm.Xt[slot][hs];
+        const unsigned char *Bs = sm.Bt[slot];
+        bf16x8 XT[2][2];      // x^T: rows p (this wave's half), K over tokens
         if constexpr (kOut) {
-            const int tl = 16 * w + c;        // token of this lane within the tile
-            // (C B^T)^T for s-blocks si <= w (this wave's 16 tokens are block w):
-            // lane (c, g) holds [s = 16 si + 4 g + i][t = 16 w + c].
-            f32x4 mt[4];
+            const unsigned char *Cs = sm.Ct[slot];
+            // (C B^T)^T blocks sb <= tb over n: lane (c, g) holds [s = 16 sb + 4 g + i][t = 16 tb + c]
+            f32x4 G[4][4];
 #pragma unroll
-            for (int si = 0; si < 4; ++si) {
-                mt[si] = zero4;
-                if (si <= w) {
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 CF[4], BF[4];
 #pragma unroll
-                    for (int ks = 0; ks < 4; ++ks) {
-                        const bf16x8 av = *reinterpret_cast<const bf16x8 *>(
-                            sm.Bt + (16 * si + c) * kBRow + (32 * ks + 8 * g) * 2);
-                        mt[si] = mfma32(av, cop[ks], mt[si]);
+                for (int tb = 0; tb < 4; ++tb) {
+                    CF[tb] = n_operand(Cs, kCRow, 16 * tb + c, kk, g);
+                    BF[tb] = n_operand_b(Bs, 16 * tb + c, kk, g);
+                }
+#pragma unroll
+                for (int sb = 0; sb < 4; ++sb)
+#pragma unroll
+                    for (int tb = sb; tb < 4; ++tb)
+                        G[sb][tb] = mfma32(BF[sb], CF[tb], kk == 0 ? zero4 : G[sb][tb]);
+            }
+            sched_fence();
+            float lamt[4];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb)
+                lamt[tb] = sm.lam[w][16 * tb + c];
+            // Mask and decay, B-operand over tokens s (slot 4 h + i <-> s = 32 jj + 16 h + 4 g + i):
+            //   s in an earlier 16-block: exp(Lam_t - Lam_q) * [exp(Lam_q - Lam_s) dt_s]
+            //   s in t's 16-block      : exp(Lam_t - Lam_s) dt_s for s <= t (exponent
+            //                            masked to -inf above the diagonal), + D_h at s = t
+            bf16x8 MOP[4][2];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int sb = 2 * jj + hh;
+                        f32x4 v = zero4;
+                        if (sb < tb) {
+                            const float u = fast_exp2(lamt[tb] - sm.lam[w][16 * sb + 15]);
+                            const f32x4 vt = *reinterpret_cast<const f32x4 *>(&sm.vt[w][16 * sb + 4 * g]);
+                            v = G[sb][tb] * (vt * u);
+                        } else if (sb == tb) {
+                            const f32x4 lsv = *reinterpret_cast<const f32x4 *>(&sm.lam[w][16 * sb + 4 * g]);
+                            const f32x4 ds = *reinterpret_cast<const f32x4 *>(&sm.dtv[w][16 * sb + 4 * g]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const bool causal = 4 * g + i <= c;
+                                const float e = fast_exp2(causal ? lamt[tb] - lsv[i] : -INFINITY);
+                                v[i] = G[sb][tb][i] * e * ds[i] + ((4 * g + i == c) ? Dh : 0.f);
+                            }
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            MOP[tb][jj][4 * hh + i] = (__bf16)v[i];
                     }
                 }
             }
-            // Decay exp(Lam_t - Lam_s) dt_s under the static causal mask.  For an
-            // earlier 16-token block it factorises through that block's last
-            // token q: exp(Lam_t - Lam_q) (one exp per block per lane) times the
-            // per-token table exp(Lam_q - Lam_s) dt_s; both factors are <= 1.
-            // The diagonal block takes exp(Lam_t - Lam_s) directly and masks
-            // s > t to zero before any exponential is formed.
-            const float lamt = sm.lam[tl];
-            bf16x8 mop[2];
+            sched_fence();
+            // Y^T[p][t] = 2^ls exp(Lam_t) sum_n Z[p][n] C[t][n]   (A = Z straight from the accumulators)
+            f32x4 Y[2][4];
 #pragma unroll
-            for (int si = 0; si < 4; ++si) {
-                f32x4 v = zero4;
-                if (si < w) {
-                    const float f = __expf(lamt - sm.lam[16 * si + 15]);
-                    const f32x4 ev = *reinterpret_cast<const f32x4 *>(&sm.ed[16 * si + 4 * g]);
-                    v = mt[si] * (ev * f);
-                } else if (si == w) {
-                    const f32x4 lv = *reinterpret_cast<const f32x4 *>(&sm.lam[16 * si + 4 * g]);
-                    const f32x4 dv = *reinterpret_cast<const f32x4 *>(&sm.dtv[16 * si + 4 * g]);
+            for (int kk = 0; kk < 4; ++kk) {
+                bf16x8 CF[4];
 #pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        v[i] = (4 * g + i <= c) ? mt[si][i] * __expf(lamt - lv[i]) * dv[i] : 0.f;
+                for (int tb = 0; tb < 4; ++tb)
+                    CF[tb] = n_operand(Cs, kCRow, 16 * tb + c, kk, g);
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    bf16x8 za;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        za[i] = (__bf16)Z[2 * kk][q][i];
+                        za[4 + i] = (__bf16)Z[2 * kk + 1][q][i];
+                    }
+#pragma unroll
+                    for (int tb = 0; tb < 4; ++tb)
+                        Y[q][tb] = mfma32(za, CF[tb], kk == 0 ? zero4 : Y[q][tb]);
                 }
-#pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    mop[si >> 1][(si & 1) * 4 + i] = (__bf16)v[i];
             }
-            // Y^T[p][t] = sum_s x^T[p][s] Lmask[s][t]   (diagonal tile)
-            f32x4 yacc[4];
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi) {
-                yacc[pi] = mfma32(tr_operand(sm.Xt, kXRow, 0, 16 * pi, g, c), mop[0], zero4);
-                if (w >= 2)
-                    yacc[pi] = mfma32(tr_operand(sm.Xt, kXRow, 1, 16 * pi, g, c), mop[1], yacc[pi]);
+            for (int tb = 0; tb < 4; ++tb) {
+                const float dec = fast_exp2(lamt[tb] + md.ly);
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    Y[q][tb] *= dec;
             }
-            // + exp(Lam_t - Lam_e) R_old C^T   (earlier tiles and earlier chunks)
-            const float dec_in = __expf(lamt - sm.scal[0]);
+            sched_fence();
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi) {
-                f32x4 yo = zero4;
+            for (int q = 0; q < 2; ++q)
 #pragma unroll
-                for (int ks = 0; ks < 4; ++ks) {
-                    const bf16x8 av = *reinterpret_cast<const bf16x8 *>(
-                        sm.Sb + (16 * pi + c) * kSRow + (32 * ks + 8 * g) * 2);
-                    yo = mfma32(av, cop[ks], yo);
+                for (int jj = 0; jj < 2; ++jj)
+                    XT[q][jj] = tr_operand(Xs, kXRow, jj, 32 * ph + 16 * q, g, c);
+            // Y^T += x^T (masked C B^T)^T over the causal token blocks, then y = bf16(Y)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int tb = 0; tb < 4; ++tb) {
+                    Y[q][tb] = mfma32(XT[q][0], MOP[tb][0], Y[q][tb]);
+                    if (tb >= 2)
+                        Y[q][tb] = mfma32(XT[q][1], MOP[tb][1], Y[q][tb]);
                 }
-                yacc[pi] += yo * dec_in;
-            }
-            // y = Y + D_h x, one rounding to bf16.
+            if (active) {
+                __bf16 *yt = ybase + t0 * ystride;
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi) {
-                const bf16x4 xv = *reinterpret_cast<const bf16x4 *>(
-                    sm.Xt + tl * kXRow + (16 * pi + 4 * g) * 2);
+                for (int tb = 0; tb < 4; ++tb) {
+                    if (t0 + 16 * tb + c < L) {
+                        __bf16 *yp = yt + (16 * tb + c) * ystride;
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    yout[pi][i] = (__bf16)(yacc[pi][i] + Dh * (float)xv[i]);
-            }
-        }
-    };
-    auto write_sb = [&]() {
-        if constexpr (kOut) {
+                        for (int q = 0; q < 2; ++q) {
+                            bf16x4 yv;
 #pragma unroll
-            for (int ni = 0; ni < 2; ++ni)
-#pragma unroll
-                for (int pi = 0; pi < 4; ++pi) {
-                    bf16x4 v;
-#pragma unroll
-                    for (int i = 0; i < 4; ++i)
-                        v[i] = (__bf16)R[ni][pi][i];
-                    *reinterpret_cast<bf16x4 *>(sm.Sb + (16 * pi + c) * kSRow +
-                                                (32 * w + 16 * ni + 4 * g) * 2) = v;
+                            for (int i = 0; i < 4; ++i)
+                                yv[i] = (__bf16)Y[q][tb][i];
+                            *reinterpret_cast<bf16x4 *>(yp + 16 * q) = yv;
+                        }
+                    }
                 }
-        }
-    };
-    auto store_y = [&](const bf16x4 (&yv)[4], int64_t t0y) {
-        const int64_t t = t0y + 16 * w + c;
-        if (t < L) {
-            __bf16 *yp = io.y + t * io.xstride + 4 * g;
+            }
+        } else {
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi)
-                *reinterpret_cast<bf16x4 *>(yp + 16 * pi) = yv[pi];
+            for (int q = 0; q < 2; ++q)
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj)
+                    XT[q][jj] = tr_operand(Xs, kXRow, jj, 32 * ph + 16 * q, g, c);
         }
+        sched_fence();
+        update_state(Bs, XT, md);
     };
 
-    if constexpr (kOut) {
-        // One tile of loads in flight; y of a tile is stored at the top of the
-        // next iteration, before that iteration's loads are issued.  The C rows
-        // are consumed from the register set before the next loads overwrite it.
-        TileRegs pre;
-        load_tile<kOut>(pre, io, tseg0, L, tid);
-        store_tile<kOut>(sm, pre, tseg0, L, a.Q, lamE, tid);
-        bf16x4 ypend[4];
-        for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
-            lds_barrier();                        // tile t0 (and Sb) visible in LDS
-            bf16x8 cop[4];
+    // Tile k is staged in ring slot k & 1 (B, C, x) and in the wave's own
+    // tables; tile k + 1's loads are in flight in `pf` while tile k is
+    // computed.  The barrier at the top of an iteration publishes the slot
+    // written at the end of the previous one and guarantees every wave is done
+    // reading the slot the current iteration will overwrite.
+    load_tile<kOut>(pf, io, tseg0, L, tid);
+    TileMode mnext = stage_tile<kOut>(sm, pf, 0, tseg0, L, Ah2, ls, lsum, tid);
+    int slot = 0;
+    for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
+        lds_barrier();
+        const TileMode md = mnext;
+        if (uniform(md.renorm)) {
 #pragma unroll
-            for (int ks = 0; ks < 4; ++ks)
-                cop[ks] = pre.c[ks];
-            if (t0 != tseg0)
-                store_y(ypend, t0 - kT);
-            load_tile<kOut>(pre, io, t0 + kT, L, tid);   // next tile (clamped past the end)
-            compute_tile(cop, ypend);
-            lds_barrier();                        // every read of this tile's LDS is done
-            write_sb();
-            if (t0 + kT < tseg1)
-                store_tile<kOut>(sm, pre, t0 + kT, L, a.Q, lamE, tid);
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    Z[nb][q] *= md.rscale;
         }
-        store_y(ypend, tseg0 + ((tseg1 - tseg0 - 1) / kT) * kT);
-    } else {
-        // State only: two tiles of loads in flight (ring of two register sets).
-        TileRegs p0, p1;
-        bf16x8 cdummy[4];
-        bf16x4 ydummy[4];
-        load_tile<kOut>(p0, io, tseg0, L, tid);
-        load_tile<kOut>(p1, io, tseg0 + kT, L, tid);
-        store_tile<kOut>(sm, p0, tseg0, L, a.Q, lamE, tid);
-        for (int64_t t0 = tseg0; t0 < tseg1; t0 += 2 * kT) {
-            // tile t0 is in LDS, p1 holds t0 + 64 (in flight), p0 is free
-            lds_barrier();
-            load_tile<kOut>(p0, io, t0 + 2 * kT, L, tid);
-            compute_tile(cdummy, ydummy);
-            lds_barrier();
-            if (t0 + kT >= tseg1)
-                break;
-            store_tile<kOut>(sm, p1, t0 + kT, L, a.Q, lamE, tid);
-            // tile t0 + 64 is in LDS, p0 holds t0 + 128 (in flight), p1 is free
-            lds_barrier();
-            load_tile<kOut>(p1, io, t0 + 3 * kT, L, tid);
-            compute_tile(cdummy, ydummy);
-            lds_barrier();
-            store_tile<kOut>(sm, p0, t0 + 2 * kT, L, a.Q, lamE, tid);
-        }
+        load_tile<kOut>(pf, io, t0 + kT, L, tid);     // next tile (clamped past the end)
+        sched_fence();
+        compute_tile(slot, md, t0);
+        slot ^= 1;
+        if (t0 + kT < tseg1)
+            mnext = stage_tile<kOut>(sm, pf, slot, t0 + kT, L, Ah2, ls, lsum, tid);
     }
 
+    if (!active)
+        return;
     float *dst = nullptr;
     if (kOut) {
         if (seg == a.nseg - 1)
             dst = a.fin + bh * kP * kN;
     } else {
         dst = a.ws_state + (bh * a.nslot + seg) * kP * kN;
-        if (tid == 0)
-            a.ws_decay[bh * a.nslot + seg] = decprod;
+        if (tid == 128 * hs)
+            a.ws_decay[bh * a.nslot + seg] = fast_exp2(lsum);
     }
     if (dst) {
+        const float sc = fast_exp2(ls);
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni)
+        for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-            for (int pi = 0; pi < 4; ++pi)
-                *reinterpret_cast<f32x4 *>(dst + (16 * pi + c) * kN + 32 * w + 16 * ni + 4 * g) =
-                    R[ni][pi];
-    }
-}
-
-// Decay preparation: for every (b, h) and token t, the chunk-referenced
-// inclusive log-decay Lam_t = sum over the chunk's tokens r <= t of dt_r A_h
-// (fp32), stored with dt_t as float2 in [B][H][L] order so that the scan
-// kernels read 64 consecutive tokens of one head as one coalesced 512-byte
-// row instead of gathering dt with a stride of H floats.  One work-group per
-// (b, chunk, 16 heads): dt of the chunk is staged in LDS with 64-byte
-// coalesced loads; each wave then scans its heads in 64-token steps (lane =
-// token), carrying the running sum across steps.
-constexpr int kPrepHeads = 16;
-constexpr int kPrepMaxQ = 512;
-
-__global__ __launch_bounds__(256) void decay_prep_kernel(const float *__restrict__ dt,
-                                                         const float *__restrict__ A,
-                                                         float2 *__restrict__ ld, int64_t L,
-                                                         int H, int Q)
-{
-    __shared__ float sdt[kPrepMaxQ][kPrepHeads + 1];
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63;
-    const int nhg = (H + kPrepHeads - 1) / kPrepHeads;
-    const int64_t nc = (L + Q - 1) / Q;
-    const int64_t j = blockIdx.x;
-    const int hg = (int)(j % nhg);
-    const int64_t c = (j / nhg) % nc;
-    const int64_t b = j / (nhg * nc);
-    const int64_t t0 = c * Q;
-    const int qc = (int)((L - t0 < Q) ? (L - t0) : Q);
-    const int h0 = hg * kPrepHeads;
-    for (int e = tid; e < qc * kPrepHeads; e += 256) {
-        const int t = e / kPrepHeads, hh = e % kPrepHeads;
-        sdt[t][hh] = (h0 + hh < H) ? dt[(b * L + t0 + t) * H + h0 + hh] : 0.f;
-    }
-    __syncthreads();
-    for (int hh = w; hh < kPrepHeads && h0 + hh < H; hh += 4) {
-        const int h = h0 + hh;
-        const float Ah = A[h];
-        float carry = 0.f;
-        float2 *out = ld + ((b * H + h) * L + t0);
-        for (int k0 = 0; k0 < qc; k0 += 64) {
-            const float d = (k0 + l < qc) ? sdt[k0 + l][hh] : 0.f;
-            const float lam = carry + wave_inclusive_sum(d * Ah, l);
-            if (k0 + l < qc)
-                out[k0 + l] = make_float2(lam, d);
-            carry = lane_f(lam, 63);
-        }
+            for (int q = 0; q < 2; ++q)
+                *reinterpret_cast<f32x4 *>(dst + (32 * ph + 16 * q + c) * kN + 16 * nb + 4 * g) =
+                    Z[nb][q] * sc;
     }
 }
 
 // Kernel 1: end state of segments 0 .. nseg-2 from a zero start.
-__global__ __launch_bounds__(kThreads, 2) void seg_state_kernel(SegArgs a)
+__global__ __launch_bounds__(kThreads, 1) void seg_state_kernel(SegArgs a)
 {
-    __shared__ TileSmem<false> sm;
+    __shared__ ScanSmem<false> sm;
     seg_body<false>(a, sm);
 }
 
 // Kernel 3: y of every segment from its entering state, and the final state.
-__global__ __launch_bounds__(kThreads, 2) void chunk_scan_kernel(SegArgs a)
+__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(SegArgs a)
 {
-    __shared__ TileSmem<true> sm;
+    __shared__ ScanSmem<true> sm;
     seg_body<true>(a, sm);
 }
 
@@ -690,6 +720,8 @@ int64_t env_int(const char *name, int64_t dflt)
     return x > 0 ? (int64_t)x : dflt;
 }
 
+constexpr int64_t kCUs = 256;
+
 }  // namespace
 
 static size_t align256(size_t n)
@@ -697,21 +729,41 @@ static size_t align256(size_t n)
     return (n + 255) / 256 * 256;
 }
 
-Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t Q)
+Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
 {
     Bf16Plan p{};
     p.nchunks = (L + Q - 1) / Q;
-    const int64_t bh = std::max<int64_t>(B * H, 1);
-    // Segments per sequence: enough work-groups to fill 256 CUs a few times over.
-    const int64_t target = env_int("SSD_SEG_TARGET_WG", 1024);
-    int64_t nseg = std::max<int64_t>(1, std::min<int64_t>(p.nchunks, (target + bh - 1) / bh));
+    const int64_t hg = G > 0 ? H / G : 1;
+    p.quads = std::max<int64_t>(1, G * ((hg + kHeads - 1) / kHeads));
+    const int64_t per_seg = std::max<int64_t>(1, B * p.quads);     // work-groups per segment
+    // Segments per sequence.  Kernel 3 runs one work-group per CU, so its time
+    // is ~ rounds * chunks per segment; kernel 1 (half the work per tile, two
+    // work-groups per CU) re-reads x for all but the last segment, and every
+    // segment adds a state round trip through the workspace.
+    int64_t nseg = env_int("SSD_NSEG", 0);
+    if (nseg <= 0) {
+        double best = 1e300;
+        for (int64_t k = 1; k <= std::max<int64_t>(p.nchunks, 1); ++k) {
+            const int64_t cps = (p.nchunks + k - 1) / k;
+            const int64_t ns = (p.nchunks + cps - 1) / cps;
+            if (ns != k)
+                continue;
+            const double r3 = (double)((per_seg * ns + kCUs - 1) / kCUs);
+            const double r1 = (double)((per_seg * (ns - 1) + 2 * kCUs - 1) / (2 * kCUs));
+            const double cost = (r3 + 0.5 * r1) * (double)cps + 0.5 * (double)ns;
+            if (cost < best) {
+                best = cost;
+                nseg = ns;
+            }
+        }
+    }
+    nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, std::max<int64_t>(p.nchunks, 1)));
     p.chunks_per_seg = std::max<int64_t>(1, (p.nchunks + nseg - 1) / nseg);
     p.nseg = std::max<int64_t>(1, (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg);
     p.nslot = p.nseg > 1 ? p.nseg : 0;
     p.state_bytes = (size_t)(B * H * p.nslot) * kP * kN * sizeof(float);
     p.decay_bytes = (size_t)(B * H * p.nslot) * sizeof(float);
-    p.ld_bytes = (size_t)(B * H * L) * sizeof(float2);
-    p.ws_bytes = align256(p.state_bytes) + align256(p.decay_bytes) + align256(p.ld_bytes);
+    p.ws_bytes = align256(p.state_bytes) + align256(p.decay_bytes);
     return p;
 }
 
@@ -735,8 +787,9 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     a.L = L;
     a.H = (int)H;
     a.G = (int)G;
-    a.Q = (int)Q;
-    a.cps = (int)plan.chunks_per_seg;
+    a.hg = (int)(H / G);
+    a.nq = (int)((a.hg + kHeads - 1) / kHeads);
+    a.seg_tokens = plan.chunks_per_seg * Q;
     a.nseg = (int)plan.nseg;
     a.nslot = (int)plan.nslot;
     const bool alias = init != nullptr && init == fin;
@@ -744,22 +797,13 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     char *wsb = static_cast<char *>(ws);
     a.ws_state = reinterpret_cast<float *>(wsb);
     a.ws_decay = reinterpret_cast<float *>(wsb + align256(plan.state_bytes));
-    float2 *ld = reinterpret_cast<float2 *>(wsb + align256(plan.state_bytes) +
-                                            align256(plan.decay_bytes));
-    a.ld = ld;
+    const int64_t per_seg = B * G * a.nq;
     hipError_t e = log_begin(log, s);
     if (e != hipSuccess)
         return e;
-    {
-        const int64_t nhg = (H + kPrepHeads - 1) / kPrepHeads;
-        decay_prep_kernel<<<(unsigned)(B * plan.nchunks * nhg), 256, 0, s>>>(dt, A, ld, L, (int)H,
-                                                                           (int)Q);
-        if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "decay_prep_kernel", s)) != hipSuccess)
-            return e;
-    }
     if (plan.nseg > 1) {
         a.nseg_launch = a.nseg - 1;
-        seg_state_kernel<<<(unsigned)(B * H * (plan.nseg - 1)), kThreads, 0, s>>>(a);
+        seg_state_kernel<<<(unsigned)(per_seg * (plan.nseg - 1)), kThreads, 0, s>>>(a);
         if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "seg_state_kernel", s)) != hipSuccess)
             return e;
         const int64_t n = B * H * (kP * kN / 4);
@@ -769,7 +813,7 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
             return e;
     }
     a.nseg_launch = a.nseg;
-    chunk_scan_kernel<<<(unsigned)(B * H * plan.nseg), kThreads, 0, s>>>(a);
+    chunk_scan_kernel<<<(unsigned)(per_seg * plan.nseg), kThreads, 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return log_kernel(log, "chunk_scan_kernel", s);

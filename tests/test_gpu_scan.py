@@ -169,10 +169,10 @@ def test_groups(H, G):
     full_check(w)
 
 
-@pytest.mark.parametrize("target", ["1", "4096"])
-def test_segment_count_extremes(target, monkeypatch):
-    """One segment per sequence, and one segment per chunk."""
-    monkeypatch.setenv("SSD_SEG_TARGET_WG", target)
+@pytest.mark.parametrize("nseg", ["1", "2", "4096"])
+def test_segment_count_extremes(nseg, monkeypatch):
+    """One segment per sequence, two, and one segment per chunk."""
+    monkeypatch.setenv("SSD_NSEG", nseg)
     w = si.small_workload(batch=2, seqlen=2048 + 77, nheads=2, chunk=64, seed=5)
     full_check(w)
 
