@@ -73,15 +73,16 @@ constexpr int kP = 64, kN = 128, kT = 64;     // headdim, dstate, tile tokens
 constexpr int kHeads = 4;                     // heads per work-group
 constexpr int kWaves = 2 * kHeads;            // two waves (P halves) per head
 constexpr int kThreads = 64 * kWaves;
-// LDS row pitches (bytes).  x is read only by transpose reads: a 32-byte pad
-// spreads the rows one read touches over all banks.  C is read only row-major
-// (8 bytes at n = 32 kk + 4 g per lane, rows 16 tb + c): a 16-byte pad does it.
-// B is read both ways, which no single pitch serves, so its rows are unpadded
-// and their 16-byte chunks are permuted by an XOR with bswz(row), which makes
-// both read patterns conflict-free.
+// LDS row pitches (bytes).  C is read only row-major (8 bytes at n = 32 kk +
+// 4 g per lane, rows 16 tb + c): a 16-byte pad spreads that over all banks.
+// B is read both row-major and by transpose reads, which no single pitch
+// serves, so its rows are unpadded and their 16-byte chunks are permuted by an
+// XOR with bswz(row), which makes both patterns conflict-free; x (transpose
+// reads only) is unpadded and permuted by xswz(row) the same way.
 constexpr int kBRow = kN * 2;                 // B tile [s][n], swizzled
 constexpr int kCRow = kN * 2 + 16;            // C tile [t][n]
-constexpr int kXRow = kP * 2 + 32;            // x tile [s][p]
+constexpr int kXRow = kP * 2;                 // x tile [s][p], swizzled
+constexpr int kGBlocks = 10;                  // causal 16 x 16 blocks of a 64-token tile
 constexpr float kLog2e = 1.4426950408889634f;
 
 template <bool kOut> struct ScanSmem;
@@ -89,6 +90,7 @@ template <> struct __align__(16) ScanSmem<true> {
     unsigned char Bt[2][kT * kBRow];          // B[s][n], ring of two tiles
     unsigned char Ct[2][kT * kCRow];          // C[t][n]
     unsigned char Xt[2][kHeads][kT * kXRow];  // x[s][p] of each head
+    f32x4 Gs[kGBlocks][64];                   // (C B^T)^T blocks of the tile, MFMA fragment order
     float lam[kWaves][kT];                    // log2(e) Lam_s, tile-referenced
     float dtv[kWaves][kT];                    // dt_s (0 past the end)
     float vt[kWaves][kT];                     // exp(Lam_q - Lam_s) dt_s, q = last token of s's 16-block
@@ -203,6 +205,28 @@ __device__ __forceinline__ int boff(int row, int n)
     return row * kBRow + (((n >> 3) ^ bswz(row)) << 4) + (n & 7) * 2;
 }
 
+__device__ __forceinline__ int xswz(int row)
+{
+    return row & 7;
+}
+
+// tr_operand on the swizzled x tile (the swizzle repeats every 8 rows).
+__device__ __forceinline__ bf16x8 tr_operand_x(const unsigned char *tile, int j, int col0, int g,
+                                               int c)
+{
+    const int row = 32 * j + 4 * g + (c >> 2), n = col0 + 4 * (c & 3);
+    const unsigned char *p = tile + row * kXRow + (((n >> 3) ^ xswz(row)) << 4) + (n & 7) * 2;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)p);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4 *)(p + 16 * kXRow));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Index of the causal block (sb <= tb) in the shared block array.
+constexpr int gblock(int sb, int tb)
+{
+    return sb * 4 - sb * (sb - 1) / 2 + (tb - sb);
+}
+
 // tr_operand on the swizzled B tile (the row's swizzle repeats every 16 rows,
 // so the upper half of the operand sits 16 rows further down unchanged).
 __device__ __forceinline__ bf16x8 tr_operand_b(const unsigned char *tile, int j, int col0, int g,
@@ -260,35 +284,68 @@ struct WaveIo {
 // prefetched tile stays in flight while the current one is computed.  t0 may
 // lie past the end of the segment: the caller then never stages that tile.
 // Offsets are 32-bit (a tile spans at most 64 rows of H*P or G*N elements).
-template <bool kOut>
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+// Buffer resource over [base, base + bytes) (raw, 32-bit data: the gfx9-family
+// descriptor word).  Buffer loads past `bytes` return zero and stores there are
+// dropped, so one descriptor per tile, ending after the last valid row, both
+// bounds and zero-fills a ragged tile without any per-lane arithmetic.
+__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
+{
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
+                                             (int)(bytes > 0 ? bytes : 0), 0x00020000);
+}
+
+// Bytes from a tile's first row to the end of its last valid row.
+__device__ __forceinline__ int64_t tile_bytes(int64_t rows, int64_t pitch, int64_t row_bytes)
+{
+    return rows > 0 ? (rows - 1) * pitch + row_bytes : 0;
+}
+
+// Issue the global loads of the tile starting at t0, through buffer resources
+// that end at the last valid token, so a ragged tile reads zeros and a tile
+// past the end of the sequence reads nothing.  Always the same instructions
+// with no branches, so the compiler's wait-count analysis sees exactly which
+// loads are outstanding and a prefetched tile stays in flight while the
+// current one is computed.  kPart: 1 = B, C and dt; 2 = x; 3 = all of them.
+template <bool kOut, int kPart = 3>
 __device__ __forceinline__ void load_tile(Prefetch<kOut> &pf, const WaveIo &io, int64_t t0,
                                           int64_t L, int tid)
 {
     const int l = tid & 63, pt = tid & 127;
-    t0 = (t0 < L) ? t0 : ((L - 1) / kT) * kT;
-    const int last = (int)((L - t0 < kT) ? (L - t0) : kT) - 1;   // last valid row
-    const __bf16 *Bp = io.B + t0 * io.bstride;
-    const __bf16 *Cp = io.C + t0 * io.bstride;
-    const __bf16 *xp = io.x + t0 * io.xstride;
-    const int bs = (int)io.bstride, xs = (int)io.xstride;
+    const int64_t rows = std::min<int64_t>(L - t0, kT);
+    const int64_t tb0 = (t0 < L) ? t0 : 0;                   // a valid base when nothing is read
+    if constexpr ((kPart & 1) != 0) {
+        const int64_t bp = io.bstride * 2;
+        const rsrc_t rb = make_rsrc(io.B + tb0 * io.bstride, tile_bytes(rows, bp, kN * 2));
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int off = std::min((tid >> 4) + 32 * r, last) * bs + (tid & 15) * 8;
-        pf.b[r] = *reinterpret_cast<const uint4 *>(Bp + off);
-        if constexpr (kOut)
-            pf.c[r] = *reinterpret_cast<const uint4 *>(Cp + off);
-    }
+        for (int r = 0; r < 2; ++r) {
+            const unsigned off = (unsigned)((tid >> 4) + 32 * r) * (unsigned)bp + (tid & 15) * 16u;
+            pf.b[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
+        }
+        if constexpr (kOut) {
+            const rsrc_t rc = make_rsrc(io.C + tb0 * io.bstride, tile_bytes(rows, bp, kN * 2));
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int off = std::min((pt >> 3) + 16 * r, last) * xs + (pt & 7) * 8;
-        pf.x[r] = *reinterpret_cast<const uint4 *>(xp + off);
+            for (int r = 0; r < 2; ++r) {
+                const unsigned off = (unsigned)((tid >> 4) + 32 * r) * (unsigned)bp + (tid & 15) * 16u;
+                pf.c[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
+            }
+        }
+        const int64_t dp = (int64_t)io.dtstride * 4;
+        const rsrc_t rd = make_rsrc(io.dt + tb0 * io.dtstride, tile_bytes(rows, dp, 4));
+        pf.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (unsigned)l * (unsigned)dp, 0, 0));
     }
-    pf.dt = io.dt[t0 * io.dtstride + std::min(l, last) * io.dtstride];
-}
-
-__device__ __forceinline__ uint4 masked(uint4 v, unsigned m)
-{
-    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+    if constexpr ((kPart & 2) != 0) {
+        const int64_t xp = io.xstride * 2;
+        const rsrc_t rx = make_rsrc(io.x + tb0 * io.xstride, tile_bytes(rows, xp, kP * 2));
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const unsigned off = (unsigned)((pt >> 3) + 16 * r) * (unsigned)xp + (pt & 7) * 16u;
+            pf.x[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
+        }
+    }
 }
 
 // The state is held scaled: R = 2^ls Z with a wave-uniform ls in [-kRenorm, 0].
@@ -297,6 +354,13 @@ __device__ __forceinline__ uint4 masked(uint4 v, unsigned m)
 // only when ls would fall below -kRenorm, and a tile whose own decay exceeds
 // that is applied to Z directly.  Every factor formed stays within 2^(2 kRenorm).
 constexpr float kRenorm = 48.f;
+
+// The wave's index in the work-group, as a scalar: everything derived from it
+// (head, pointers, buffer descriptors) then stays in scalar registers.
+__device__ __forceinline__ int wave_id()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
 
 // Keeps the instruction scheduler from moving work across this point, so that
 // the registers of one phase of a tile are not held live through another.
@@ -329,28 +393,22 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut> &sm, Prefetch<kOut
                                                int64_t t0, int64_t L, float Ah2, float &ls,
                                                float &lsum, int tid)
 {
-    const int w = tid >> 6, l = tid & 63, pt = tid & 127;
-    const int rem = (int)((L - t0 < kT) ? (L - t0) : kT);
-    // Rows past the end are zeroed with an integer mask (a conditional choice
-    // between two uint4 aggregates would be lowered to a choice of addresses
-    // and keep the prefetch registers from being promoted out of memory).
+    const int w = wave_id(), l = tid & 63, pt = tid & 127;
+    // (rows past the end were loaded as zeros)
 #pragma unroll
     for (int r = 0; r < 2; ++r) {
         const int row = (tid >> 4) + 32 * r, col = tid & 15;
-        const unsigned m = row < rem ? ~0u : 0u;
-        *reinterpret_cast<uint4 *>(sm.Bt[slot] + row * kBRow + ((col ^ bswz(row)) << 4)) =
-            masked(pf.b[r], m);
+        *reinterpret_cast<uint4 *>(sm.Bt[slot] + row * kBRow + ((col ^ bswz(row)) << 4)) = pf.b[r];
         if constexpr (kOut)
-            *reinterpret_cast<uint4 *>(sm.Ct[slot] + row * kCRow + col * 16) = masked(pf.c[r], m);
+            *reinterpret_cast<uint4 *>(sm.Ct[slot] + row * kCRow + col * 16) = pf.c[r];
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int row = (pt >> 3) + 16 * r;
-        const unsigned m = row < rem ? ~0u : 0u;
-        *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow + (pt & 7) * 16) =
-            masked(pf.x[r], m);
+        *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow +
+                                   (((pt & 7) ^ xswz(row)) << 4)) = pf.x[r];
     }
-    const float dtl = l < rem ? pf.dt : 0.f;
+    const float dtl = pf.dt;
     const float lam = wave_inclusive_sum(dtl * Ah2, l);
     const float lam_end = lane_f(lam, 63);
     lsum += lam_end;
@@ -393,7 +451,7 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut> &sm, Prefetch<kOut
 template <bool kOut>
 __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
 {
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c = l & 15;
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     const int hs = w >> 1;                                // head slot in the work-group
     const int ph = w & 1;                                 // P half: p = 32 ph .. 32 ph + 31
     const int64_t j = xcd_remap(blockIdx.x, gridDim.x);
@@ -422,9 +480,11 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
     io.B = a.B + (b * L * a.G + grp) * kN;
     io.C = a.C + (b * L * a.G + grp) * kN;
     io.dt = a.dt + b * L * a.H + h;
-    // y of lane (c, g) in token block tb: row 16 tb + c, columns 16 (2 ph + q) + 4 g .. +3
+    // y of lane (c, g) in token block tb: row 16 tb + c, columns 16 (2 ph + q) + 4 g .. +3;
+    // byte offsets from the tile's first row (a tile spans 64 rows of H * P elements)
     const int64_t ystride = (int64_t)a.H * kP;
-    __bf16 *ybase = kOut ? a.y + (b * L * a.H + h) * kP + 32 * ph + 4 * g : nullptr;
+    __bf16 *ybase = kOut ? a.y + (b * L * a.H + h) * kP : nullptr;
+    const unsigned ylane = ((unsigned)c * (unsigned)ystride + 32u * ph + 4u * g) * 2u;
 
     // State accumulators: Z[nb][q][i] = R[p = 32 ph + 16 q + c][n = 16 nb + 4 g + i] / 2^ls.
     f32x4 Z[8][2];
@@ -451,6 +511,16 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
 
     // R <- zscale R + B^T (w dt x):  A = B^T (rows n), B = scaled x (columns p)
     auto update_state = [&](const unsigned char *Bs, const bf16x8 (&XT)[2][2], const TileMode &md) {
+        // B^T operands are read ahead of their MFMAs (all of them in kernel 1; in
+        // kernel 3, whose prefetched tile is live here, half at a time), so that
+        // their LDS latency overlaps the x scaling and the previous half's MFMAs.
+        constexpr int kAhead = kOut ? 4 : 8;
+        bf16x8 BT[8][2];
+#pragma unroll
+        for (int nb = 0; nb < kAhead; ++nb) {
+            BT[nb][0] = tr_operand_b(Bs, 0, 16 * nb, g, c);
+            BT[nb][1] = tr_operand_b(Bs, 1, 16 * nb, g, c);
+        }
         f32x4 wv[2][2];
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj)
@@ -474,11 +544,13 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
         }
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb) {
-            const bf16x8 b0 = tr_operand_b(Bs, 0, 16 * nb, g, c);
-            const bf16x8 b1 = tr_operand_b(Bs, 1, 16 * nb, g, c);
+            if (nb + kAhead < 8) {
+                BT[nb + kAhead][0] = tr_operand_b(Bs, 0, 16 * (nb + kAhead), g, c);
+                BT[nb + kAhead][1] = tr_operand_b(Bs, 1, 16 * (nb + kAhead), g, c);
+            }
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                Z[nb][q] = mfma32(b1, XS[q][1], mfma32(b0, XS[q][0], Z[nb][q]));
+                Z[nb][q] = mfma32(BT[nb][1], XS[q][1], mfma32(BT[nb][0], XS[q][0], Z[nb][q]));
         }
     };
 
@@ -490,61 +562,26 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
         bf16x8 XT[2][2];      // x^T: rows p (this wave's half), K over tokens
         if constexpr (kOut) {
             const unsigned char *Cs = sm.Ct[slot];
-            // (C B^T)^T blocks sb <= tb over n: lane (c, g) holds [s = 16 sb + 4 g + i][t = 16 tb + c]
-            f32x4 G[4][4];
+            // (C B^T)^T causal blocks, shared by the four heads: wave w computes
+            // blocks w and w + 8 of the ten; lane (c, g) of block (sb, tb) holds
+            // [s = 16 sb + 4 g + i][t = 16 tb + c].
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) {
-                bf16x8 CF[4], BF[4];
+            for (int bi0 = 0; bi0 < kGBlocks; bi0 += kWaves) {
+                const int bi = bi0 + w;
+                if (bi < kGBlocks) {
+                    const int sb = bi < 4 ? 0 : bi < 7 ? 1 : bi < 9 ? 2 : 3;
+                    const int tb = bi - gblock(sb, sb) + sb;
+                    f32x4 gacc = zero4;
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    CF[tb] = n_operand(Cs, kCRow, 16 * tb + c, kk, g);
-                    BF[tb] = n_operand_b(Bs, 16 * tb + c, kk, g);
-                }
-#pragma unroll
-                for (int sb = 0; sb < 4; ++sb)
-#pragma unroll
-                    for (int tb = sb; tb < 4; ++tb)
-                        G[sb][tb] = mfma32(BF[sb], CF[tb], kk == 0 ? zero4 : G[sb][tb]);
-            }
-            sched_fence();
-            float lamt[4];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb)
-                lamt[tb] = sm.lam[w][16 * tb + c];
-            // Mask and decay, B-operand over tokens s (slot 4 h + i <-> s = 32 jj + 16 h + 4 g + i):
-            //   s in an earlier 16-block: exp(Lam_t - Lam_q) * [exp(Lam_q - Lam_s) dt_s]
-            //   s in t's 16-block      : exp(Lam_t - Lam_s) dt_s for s <= t (exponent
-            //                            masked to -inf above the diagonal), + D_h at s = t
-            bf16x8 MOP[4][2];
-#pragma unroll
-            for (int tb = 0; tb < 4; ++tb) {
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj) {
-#pragma unroll
-                    for (int hh = 0; hh < 2; ++hh) {
-                        const int sb = 2 * jj + hh;
-                        f32x4 v = zero4;
-                        if (sb < tb) {
-                            const float u = fast_exp2(lamt[tb] - sm.lam[w][16 * sb + 15]);
-                            const f32x4 vt = *reinterpret_cast<const f32x4 *>(&sm.vt[w][16 * sb + 4 * g]);
-                            v = G[sb][tb] * (vt * u);
-                        } else if (sb == tb) {
-                            const f32x4 lsv = *reinterpret_cast<const f32x4 *>(&sm.lam[w][16 * sb + 4 * g]);
-                            const f32x4 ds = *reinterpret_cast<const f32x4 *>(&sm.dtv[w][16 * sb + 4 * g]);
-#pragma unroll
-                            for (int i = 0; i < 4; ++i) {
-                                const bool causal = 4 * g + i <= c;
-                                const float e = fast_exp2(causal ? lamt[tb] - lsv[i] : -INFINITY);
-                                v[i] = G[sb][tb][i] * e * ds[i] + ((4 * g + i == c) ? Dh : 0.f);
-                            }
-                        }
-#pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            MOP[tb][jj][4 * hh + i] = (__bf16)v[i];
-                    }
+                    for (int kk = 0; kk < 4; ++kk)
+                        gacc = mfma32(n_operand_b(Bs, 16 * sb + c, kk, g),
+                                      n_operand(Cs, kCRow, 16 * tb + c, kk, g), gacc);
+                    sm.Gs[bi][l] = gacc;
                 }
             }
-            sched_fence();
+            // x of the next tile goes out now, so that its registers are not
+            // live across the C B^T blocks.
+            load_tile<kOut, 2>(pf, io, t0 + kT, L, tid);
             // Y^T[p][t] = 2^ls exp(Lam_t) sum_n Z[p][n] C[t][n]   (A = Z straight from the accumulators)
             f32x4 Y[2][4];
 #pragma unroll
@@ -566,19 +603,56 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
                         Y[q][tb] = mfma32(za, CF[tb], kk == 0 ? zero4 : Y[q][tb]);
                 }
             }
+            float lamt[4];
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
+                lamt[tb] = sm.lam[w][16 * tb + c];
                 const float dec = fast_exp2(lamt[tb] + md.ly);
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
                     Y[q][tb] *= dec;
+            }
+            lds_barrier();                            // every block of the tile is in Gs
+            // Mask and decay, B-operand over tokens s (slot 4 h + i <-> s = 32 jj + 16 h + 4 g + i):
+            //   s in an earlier 16-block: exp(Lam_t - Lam_q) * [exp(Lam_q - Lam_s) dt_s]
+            //   s in t's 16-block      : exp(Lam_t - Lam_s) dt_s for s <= t (exponent
+            //                            masked to -inf above the diagonal), + D_h at s = t
+            bf16x8 MOP[4][2];
+#pragma unroll
+            for (int tb = 0; tb < 4; ++tb) {
+#pragma unroll
+                for (int jj = 0; jj < 2; ++jj) {
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int sb = 2 * jj + hh;
+                        f32x4 v = zero4;
+                        if (sb < tb) {
+                            const float u = fast_exp2(lamt[tb] - sm.lam[w][16 * sb + 15]);
+                            const f32x4 vt = *reinterpret_cast<const f32x4 *>(&sm.vt[w][16 * sb + 4 * g]);
+                            v = sm.Gs[gblock(sb, tb)][l] * (vt * u);
+                        } else if (sb == tb) {
+                            const f32x4 gd = sm.Gs[gblock(sb, tb)][l];
+                            const f32x4 lsv = *reinterpret_cast<const f32x4 *>(&sm.lam[w][16 * sb + 4 * g]);
+                            const f32x4 ds = *reinterpret_cast<const f32x4 *>(&sm.dtv[w][16 * sb + 4 * g]);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) {
+                                const bool causal = 4 * g + i <= c;
+                                const float e = fast_exp2(causal ? lamt[tb] - lsv[i] : -INFINITY);
+                                v[i] = gd[i] * e * ds[i] + ((4 * g + i == c) ? Dh : 0.f);
+                            }
+                        }
+#pragma unroll
+                        for (int i = 0; i < 4; ++i)
+                            MOP[tb][jj][4 * hh + i] = (__bf16)v[i];
+                    }
+                }
             }
             sched_fence();
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
-                    XT[q][jj] = tr_operand(Xs, kXRow, jj, 32 * ph + 16 * q, g, c);
+                    XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
             // Y^T += x^T (masked C B^T)^T over the causal token blocks, then y = bf16(Y)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
@@ -589,28 +663,28 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
                         Y[q][tb] = mfma32(XT[q][1], MOP[tb][1], Y[q][tb]);
                 }
             if (active) {
-                __bf16 *yt = ybase + t0 * ystride;
+                // rows past the end fall outside the descriptor and are dropped
+                const rsrc_t ry = make_rsrc(ybase + t0 * ystride,
+                                            tile_bytes(std::min<int64_t>(L - t0, kT), ystride * 2, kP * 2));
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb) {
-                    if (t0 + 16 * tb + c < L) {
-                        __bf16 *yp = yt + (16 * tb + c) * ystride;
+                for (int tb = 0; tb < 4; ++tb)
 #pragma unroll
-                        for (int q = 0; q < 2; ++q) {
-                            bf16x4 yv;
+                    for (int q = 0; q < 2; ++q) {
+                        bf16x4 yv;
 #pragma unroll
-                            for (int i = 0; i < 4; ++i)
-                                yv[i] = (__bf16)Y[q][tb][i];
-                            *reinterpret_cast<bf16x4 *>(yp + 16 * q) = yv;
-                        }
+                        for (int i = 0; i < 4; ++i)
+                            yv[i] = (__bf16)Y[q][tb][i];
+                        __builtin_amdgcn_raw_buffer_store_b64(
+                            __builtin_bit_cast(u32x2, yv), ry,
+                            ylane + 32u * tb * (unsigned)ystride + 32u * q, 0, 0);
                     }
-                }
             }
         } else {
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
                 for (int jj = 0; jj < 2; ++jj)
-                    XT[q][jj] = tr_operand(Xs, kXRow, jj, 32 * ph + 16 * q, g, c);
+                    XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
         }
         sched_fence();
         update_state(Bs, XT, md);
@@ -634,7 +708,8 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
                 for (int q = 0; q < 2; ++q)
                     Z[nb][q] *= md.rscale;
         }
-        load_tile<kOut>(pf, io, t0 + kT, L, tid);     // next tile (clamped past the end)
+        // next tile (clamped past the end); kernel 3 issues its x loads mid-tile
+        load_tile<kOut, kOut ? 1 : 3>(pf, io, t0 + kT, L, tid);
         sched_fence();
         compute_tile(slot, md, t0);
         slot ^= 1;
