@@ -39,12 +39,13 @@
 // * The next tile's global loads are issued before the current tile is
 //   computed and land in registers (software pipelining).
 // * Sequence parallelism: a (b, h) sequence is cut into segments of whole
-//   chunks.  Kernel 1 computes each segment's end state from a zero start,
-//   kernel 2 chains the segment states (S_in[k+1] = decay_k S_in[k] +
-//   S_loc[k]), kernel 3 re-walks every segment from its true entering state
-//   and writes y (and the final state).  The segment count is chosen so that
-//   kernel 3 fills the chip in as few rounds as possible while every extra
-//   segment costs one more pass of its x through HBM.
+//   chunks.  The state kernel computes each segment's end state from a zero
+//   start (segments 0 .. nseg-2); the scan kernel chains those into the state
+//   entering its own segment (S_in[k+1] = decay_k S_in[k] + S_loc[k]) and
+//   re-walks the segment from it, writing y (and the final state).  The
+//   segment count is chosen so that the scan kernel fills the chip in as few
+//   rounds as possible while every extra segment costs one more pass of its
+//   x through HBM.
 // * Work-groups are remapped so that neighbouring (batch row, segment, head
 //   quad) work lands on one XCD and shares its L2 for the B/C tiles.
 //
@@ -446,8 +447,8 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut> &sm, Prefetch<kOut
     return md;
 }
 
-// kOut = false: kernel 1 (segment end state from zero, written to the workspace).
-// kOut = true : kernel 3 (y and, for the last segment, the final state).
+// kOut = false: the state kernel (segment end state from zero, to the workspace).
+// kOut = true : the scan kernel (y and, for the last segment, the final state).
 template <bool kOut>
 __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
 {
@@ -487,13 +488,17 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
     const unsigned ylane = ((unsigned)c * (unsigned)ystride + 32u * ph + 4u * g) * 2u;
 
     // State accumulators: Z[nb][q][i] = R[p = 32 ph + 16 q + c][n = 16 nb + 4 g + i] / 2^ls.
+    const int zoff = (32 * ph + c) * kN + 4 * g;      // + 16 q kN + 16 nb
     f32x4 Z[8][2];
     {
+        // Scan kernel: the state entering the segment, chained here from the
+        // initial state and the end states of the earlier segments:
+        //   S_in[0] = init (or 0);  S_in[k+1] = decay_k S_in[k] + S_loc[k]
+        // (fp32, in segment order).  When the final state aliases the initial
+        // state, the state kernel has copied the initial state to slot nseg-1.
         const float *src = nullptr;
         if (kOut) {
-            if (seg > 0)
-                src = a.ws_state + (bh * a.nslot + (seg - 1)) * kP * kN;
-            else if (a.seg0_from_ws)
+            if (a.seg0_from_ws)
                 src = a.ws_state + (bh * a.nslot + (a.nseg - 1)) * kP * kN;
             else if (a.init)
                 src = a.init + bh * kP * kN;
@@ -502,17 +507,39 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                Z[nb][q] = src ? *reinterpret_cast<const f32x4 *>(
-                                     src + (32 * ph + 16 * q + c) * kN + 16 * nb + 4 * g)
+                Z[nb][q] = src ? *reinterpret_cast<const f32x4 *>(src + zoff + 16 * q * kN + 16 * nb)
                                : zero4;
+        if (kOut) {
+            for (int k = 0; k < seg; ++k) {
+                const float d = a.ws_decay[bh * a.nslot + k];
+                const float *sl = a.ws_state + (bh * a.nslot + k) * kP * kN;
+#pragma unroll
+                for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                    for (int q = 0; q < 2; ++q)
+                        Z[nb][q] = Z[nb][q] * d + *reinterpret_cast<const f32x4 *>(
+                                                      sl + zoff + 16 * q * kN + 16 * nb);
+            }
+        } else if (seg == 0 && a.seg0_from_ws && active) {
+            // alias of final and initial state: keep a copy of the initial state
+            const float *ini = a.init + bh * kP * kN;
+            float *cp = a.ws_state + (bh * a.nslot + (a.nseg - 1)) * kP * kN;
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    *reinterpret_cast<f32x4 *>(cp + zoff + 16 * q * kN + 16 * nb) =
+                        *reinterpret_cast<const f32x4 *>(ini + zoff + 16 * q * kN + 16 * nb);
+        }
     }
     float ls = 0.f;         // R = 2^ls Z
     float lsum = 0.f;       // log2 of the product of tile decays over the segment
 
     // R <- zscale R + B^T (w dt x):  A = B^T (rows n), B = scaled x (columns p)
     auto update_state = [&](const unsigned char *Bs, const bf16x8 (&XT)[2][2], const TileMode &md) {
-        // B^T operands are read ahead of their MFMAs (all of them in kernel 1; in
-        // kernel 3, whose prefetched tile is live here, half at a time), so that
+        // B^T operands are read ahead of their MFMAs (all of them in the state
+        // kernel; in the scan kernel, whose prefetched tile is live here, half at
+        // a time), so that
         // their LDS latency overlaps the x scaling and the previous half's MFMAs.
         constexpr int kAhead = kOut ? 4 : 8;
         bf16x8 BT[8][2];
@@ -708,7 +735,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
                 for (int q = 0; q < 2; ++q)
                     Z[nb][q] *= md.rscale;
         }
-        // next tile (clamped past the end); kernel 3 issues its x loads mid-tile
+        // next tile (nothing past the end); the scan kernel issues its x loads mid-tile
         load_tile<kOut, kOut ? 1 : 3>(pf, io, t0 + kT, L, tid);
         sched_fence();
         compute_tile(slot, md, t0);
@@ -739,51 +766,18 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
     }
 }
 
-// Kernel 1: end state of segments 0 .. nseg-2 from a zero start.
+// State kernel: end state of segments 0 .. nseg-2 from a zero start.
 __global__ __launch_bounds__(kThreads, 1) void seg_state_kernel(SegArgs a)
 {
     __shared__ ScanSmem<false> sm;
     seg_body<false>(a, sm);
 }
 
-// Kernel 3: y of every segment from its entering state, and the final state.
+// Scan kernel: y of every segment from its entering state, and the final state.
 __global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(SegArgs a)
 {
     __shared__ ScanSmem<true> sm;
     seg_body<true>(a, sm);
-}
-
-// Kernel 2: chain the segment states of every (b, h), elementwise over P x N.
-//   S_in[0] = init (or 0);  S_in[k+1] = decay_k S_in[k] + S_loc[k]
-// slot k (k < nseg-1) holds S_loc[k] on entry and S_in[k+1] on exit; when the
-// final state aliases the initial state, slot nseg-1 receives a copy of S_in[0].
-__global__ __launch_bounds__(256) void seg_pass_kernel(const float *__restrict__ init,
-                                                      float *__restrict__ ws_state,
-                                                      const float *__restrict__ ws_decay,
-                                                      int64_t BH, int nseg, int nslot,
-                                                      int seg0_to_ws)
-{
-    constexpr int PN4 = kP * kN / 4;
-    const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-    if (idx >= BH * PN4)
-        return;
-    const int64_t bh = idx / PN4;
-    const int e = (int)(idx - bh * PN4);
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (init)
-        s = reinterpret_cast<const float4 *>(init)[bh * PN4 + e];
-    float4 *base = reinterpret_cast<float4 *>(ws_state) + bh * nslot * PN4;
-    if (seg0_to_ws)
-        base[(int64_t)(nseg - 1) * PN4 + e] = s;
-    for (int k = 0; k < nseg - 1; ++k) {
-        const float d = ws_decay[bh * nslot + k];
-        const float4 v = base[(int64_t)k * PN4 + e];
-        s.x = d * s.x + v.x;
-        s.y = d * s.y + v.y;
-        s.z = d * s.z + v.z;
-        s.w = d * s.w + v.w;
-        base[(int64_t)k * PN4 + e] = s;
-    }
 }
 
 int64_t env_int(const char *name, int64_t dflt)
@@ -811,10 +805,10 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
     const int64_t hg = G > 0 ? H / G : 1;
     p.quads = std::max<int64_t>(1, G * ((hg + kHeads - 1) / kHeads));
     const int64_t per_seg = std::max<int64_t>(1, B * p.quads);     // work-groups per segment
-    // Segments per sequence.  Kernel 3 runs one work-group per CU, so its time
-    // is ~ rounds * chunks per segment; kernel 1 (half the work per tile, two
-    // work-groups per CU) re-reads x for all but the last segment, and every
-    // segment adds a state round trip through the workspace.
+    // Segments per sequence.  Both kernels run one work-group per CU, so the scan
+    // kernel's time is ~ rounds * chunks per segment; the state kernel (about
+    // half the work per tile) re-reads x for all but the last segment, and
+    // every segment adds state traffic through the workspace.
     int64_t nseg = env_int("SSD_NSEG", 0);
     if (nseg <= 0) {
         double best = 1e300;
@@ -824,7 +818,7 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
             if (ns != k)
                 continue;
             const double r3 = (double)((per_seg * ns + kCUs - 1) / kCUs);
-            const double r1 = (double)((per_seg * (ns - 1) + 2 * kCUs - 1) / (2 * kCUs));
+            const double r1 = (double)((per_seg * (ns - 1) + kCUs - 1) / kCUs);
             const double cost = (r3 + 0.5 * r1) * (double)cps + 0.5 * (double)ns;
             if (cost < best) {
                 best = cost;
@@ -880,11 +874,6 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
         a.nseg_launch = a.nseg - 1;
         seg_state_kernel<<<(unsigned)(per_seg * (plan.nseg - 1)), kThreads, 0, s>>>(a);
         if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "seg_state_kernel", s)) != hipSuccess)
-            return e;
-        const int64_t n = B * H * (kP * kN / 4);
-        seg_pass_kernel<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(
-            init, a.ws_state, a.ws_decay, B * H, a.nseg, a.nslot, a.seg0_from_ws);
-        if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "seg_pass_kernel", s)) != hipSuccess)
             return e;
     }
     a.nseg_launch = a.nseg;
