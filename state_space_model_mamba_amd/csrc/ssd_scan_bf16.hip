@@ -363,13 +363,6 @@ __device__ __forceinline__ int wave_id()
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-// Keeps the instruction scheduler from moving work across this point, so that
-// the registers of one phase of a tile are not held live through another.
-__device__ __forceinline__ void sched_fence()
-{
-    __builtin_amdgcn_sched_barrier(0);
-}
-
 // A wave-uniform condition as a scalar branch (the values it derives from are
 // wave-uniform, but the compiler cannot always prove it through the loop).
 __device__ __forceinline__ bool uniform(bool v)
@@ -674,7 +667,6 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
                     }
                 }
             }
-            sched_fence();
 #pragma unroll
             for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -713,7 +705,6 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
                 for (int jj = 0; jj < 2; ++jj)
                     XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
         }
-        sched_fence();
         update_state(Bs, XT, md);
     };
 
@@ -737,7 +728,6 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
         }
         // next tile (nothing past the end); the scan kernel issues its x loads mid-tile
         load_tile<kOut, kOut ? 1 : 3>(pf, io, t0 + kT, L, tid);
-        sched_fence();
         compute_tile(slot, md, t0);
         slot ^= 1;
         if (t0 + kT < tseg1)
