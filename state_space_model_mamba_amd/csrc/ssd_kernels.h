@@ -41,8 +41,10 @@ struct Bf16Plan {
     int64_t nchunks;       // ceil(L / Q)
     int64_t quads;         // work-groups per (batch row, segment): G * ceil(H / G / 4)
     int64_t chunks_per_seg;
-    int64_t nseg;          // segments per (b, h)
-    int64_t nslot;         // state slots per (b, h) in the workspace (0 if nseg == 1)
+    int64_t nseg;          // segments per (b, h) of the scan kernel
+    int64_t nsub;          // state-kernel units per segment (each segment but the last)
+    int64_t unit_tokens;   // tokens per unit (a multiple of 64)
+    int64_t nslot;         // state slots per (b, h): one per unit + one spare (0 if nseg == 1)
     size_t state_bytes;    // B*H*nslot*P*N*4
     size_t decay_bytes;    // B*H*nslot*4
     size_t ws_bytes;       // total workspace

@@ -120,9 +120,11 @@ struct SegArgs {
     int hg;              // heads per group
     int nq;              // work-groups (head quads) per group
     int64_t seg_tokens;  // tokens per segment (whole chunks)
+    int64_t unit_tokens; // tokens per state-kernel unit
     int nseg;            // segments per (b, h)
-    int nseg_launch;     // segments this launch covers
-    int nslot;
+    int nsub;            // state-kernel units per segment
+    int nseg_launch;     // segments (scan kernel) or units (state kernel) this launch covers
+    int nslot;           // units of segments 0 .. nseg-2, then the spare slot
     int seg0_from_ws;    // segment 0 reads its entering state from slot nseg-1
 };
 
@@ -460,8 +462,17 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
     const int h = grp * a.hg + (active ? hw : a.hg - 1);
     const int64_t bh = b * a.H + h;
     const int64_t L = a.L;
-    const int64_t tseg0 = (int64_t)seg * a.seg_tokens;
-    const int64_t tseg1 = std::min<int64_t>(L, tseg0 + a.seg_tokens);
+    // The scan kernel walks segment `seg`; the state kernel walks unit `seg`
+    // (part `seg % nsub` of segment `seg / nsub`).
+    int64_t tseg0, tseg1;
+    if (kOut) {
+        tseg0 = (int64_t)seg * a.seg_tokens;
+        tseg1 = std::min<int64_t>(L, tseg0 + a.seg_tokens);
+    } else {
+        const int64_t sbeg = (int64_t)(seg / a.nsub) * a.seg_tokens;
+        tseg0 = sbeg + (int64_t)(seg % a.nsub) * a.unit_tokens;
+        tseg1 = std::min<int64_t>(std::min<int64_t>(L, sbeg + a.seg_tokens), tseg0 + a.unit_tokens);
+    }
     const float Ah2 = a.A[h] * kLog2e;
     const float Dh = kOut ? a.D[h] : 0.f;
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
@@ -484,15 +495,18 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
     const int zoff = (32 * ph + c) * kN + 4 * g;      // + 16 q kN + 16 nb
     f32x4 Z[8][2];
     {
-        // Scan kernel: the state entering the segment, chained here from the
-        // initial state and the end states of the earlier segments:
-        //   S_in[0] = init (or 0);  S_in[k+1] = decay_k S_in[k] + S_loc[k]
-        // (fp32, in segment order).  When the final state aliases the initial
-        // state, the state kernel has copied the initial state to slot nseg-1.
+        // Scan kernel: the state entering the segment, from the initial state
+        // and the end states S_k of the earlier units (state kernel), i.e. the
+        // chain S <- d_k S + S_k written out as
+        //   S_in = (prod_k d_k) S_init + sum_k (prod_{j > k} d_j) S_k,
+        // summed from the last unit backwards so that the loads of all units
+        // are independent and can be in flight together (fp32, fixed order).
+        // When the final state aliases the initial state, the state kernel has
+        // copied the initial state to the spare slot.
         const float *src = nullptr;
         if (kOut) {
             if (a.seg0_from_ws)
-                src = a.ws_state + (bh * a.nslot + (a.nseg - 1)) * kP * kN;
+                src = a.ws_state + (bh * a.nslot + (a.nslot - 1)) * kP * kN;
             else if (a.init)
                 src = a.init + bh * kP * kN;
         }
@@ -500,23 +514,31 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
-                Z[nb][q] = src ? *reinterpret_cast<const f32x4 *>(src + zoff + 16 * q * kN + 16 * nb)
-                               : zero4;
+                Z[nb][q] = zero4;
+        float wgt = 1.f;                              // prod_{j > k} d_j
         if (kOut) {
-            for (int k = 0; k < seg; ++k) {
-                const float d = a.ws_decay[bh * a.nslot + k];
+#pragma unroll 2
+            for (int k = seg * a.nsub - 1; k >= 0; --k) {
                 const float *sl = a.ws_state + (bh * a.nslot + k) * kP * kN;
 #pragma unroll
                 for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
                     for (int q = 0; q < 2; ++q)
-                        Z[nb][q] = Z[nb][q] * d + *reinterpret_cast<const f32x4 *>(
-                                                      sl + zoff + 16 * q * kN + 16 * nb);
+                        Z[nb][q] += *reinterpret_cast<const f32x4 *>(sl + zoff + 16 * q * kN + 16 * nb) * wgt;
+                wgt *= a.ws_decay[bh * a.nslot + k];
             }
-        } else if (seg == 0 && a.seg0_from_ws && active) {
+        }
+        if (src) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    Z[nb][q] += *reinterpret_cast<const f32x4 *>(src + zoff + 16 * q * kN + 16 * nb) * wgt;
+        }
+        if (!kOut && seg == 0 && a.seg0_from_ws && active) {
             // alias of final and initial state: keep a copy of the initial state
             const float *ini = a.init + bh * kP * kN;
-            float *cp = a.ws_state + (bh * a.nslot + (a.nseg - 1)) * kP * kN;
+            float *cp = a.ws_state + (bh * a.nslot + (a.nslot - 1)) * kP * kN;
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
@@ -819,7 +841,32 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
     nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, std::max<int64_t>(p.nchunks, 1)));
     p.chunks_per_seg = std::max<int64_t>(1, (p.nchunks + nseg - 1) / nseg);
     p.nseg = std::max<int64_t>(1, (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg);
-    p.nslot = p.nseg > 1 ? p.nseg : 0;
+    // The state kernel may cut each of its segments into units to fill the
+    // chip (its cost ~ rounds * tiles per unit); every unit adds one more
+    // state to write, and the scan kernel's last segment chains (nseg-1) * nsub
+    // states before its first tile.
+    const int64_t seg_tiles = p.chunks_per_seg * Q / kT;
+    p.nsub = 1;
+    p.unit_tokens = p.chunks_per_seg * Q;
+    if (p.nseg > 1) {
+        int64_t want = env_int("SSD_NSUB", 0);
+        double best = 1e300;
+        for (int64_t k = 1; k <= 8; ++k) {
+            const int64_t ut = (seg_tiles + k - 1) / k;             // tiles per unit
+            const int64_t nk = (seg_tiles + ut - 1) / ut;           // non-empty units
+            if (nk != k)
+                continue;
+            const double rounds = (double)((per_seg * (p.nseg - 1) * nk + kCUs - 1) / kCUs);
+            // (a chained state costs the scan kernel's critical path ~ 3 tiles)
+            const double cost = rounds * (double)ut + (double)nk + 3.0 * (double)((p.nseg - 1) * nk);
+            if (want > 0 ? k == want : cost < best) {
+                best = cost;
+                p.nsub = nk;
+                p.unit_tokens = ut * kT;
+            }
+        }
+    }
+    p.nslot = p.nseg > 1 ? (p.nseg - 1) * p.nsub + 1 : 0;
     p.state_bytes = (size_t)(B * H * p.nslot) * kP * kN * sizeof(float);
     p.decay_bytes = (size_t)(B * H * p.nslot) * sizeof(float);
     p.ws_bytes = align256(p.state_bytes) + align256(p.decay_bytes);
@@ -849,7 +896,9 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     a.hg = (int)(H / G);
     a.nq = (int)((a.hg + kHeads - 1) / kHeads);
     a.seg_tokens = plan.chunks_per_seg * Q;
+    a.unit_tokens = plan.unit_tokens;
     a.nseg = (int)plan.nseg;
+    a.nsub = (int)plan.nsub;
     a.nslot = (int)plan.nslot;
     const bool alias = init != nullptr && init == fin;
     a.seg0_from_ws = (alias && plan.nseg > 1) ? 1 : 0;
@@ -861,8 +910,8 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     if (e != hipSuccess)
         return e;
     if (plan.nseg > 1) {
-        a.nseg_launch = a.nseg - 1;
-        seg_state_kernel<<<(unsigned)(per_seg * (plan.nseg - 1)), kThreads, 0, s>>>(a);
+        a.nseg_launch = (a.nseg - 1) * a.nsub;
+        seg_state_kernel<<<(unsigned)(per_seg * a.nseg_launch), kThreads, 0, s>>>(a);
         if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "seg_state_kernel", s)) != hipSuccess)
             return e;
     }

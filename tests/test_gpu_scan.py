@@ -177,6 +177,17 @@ def test_segment_count_extremes(nseg, monkeypatch):
     full_check(w)
 
 
+@pytest.mark.parametrize("nsub", ["1", "2", "5"])
+def test_state_kernel_units(nsub, monkeypatch):
+    """Segments of the state kernel cut into 1, 2 and 5 units (with a ragged
+    tail and an initial state that the final state aliases)."""
+    monkeypatch.setenv("SSD_NSEG", "3")
+    monkeypatch.setenv("SSD_NSUB", nsub)
+    w = si.small_workload(batch=2, seqlen=3 * 640 + 50, nheads=4, chunk=128, seed=21)
+    h0 = np.random.default_rng(2).standard_normal((2, 4, 64, 128)).astype(np.float32)
+    full_check(w, h0=h0)
+
+
 def test_initial_state_and_split_continuity():
     """scan(L) == scan(k) then scan(L - k, initial_state = that final state), for
     a given non-zero initial state; and final_state may alias initial_state."""
