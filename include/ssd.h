@@ -139,7 +139,7 @@ ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const float *dt, 
  *   state [B,H,P,N] fp32, updated in place: H <- alpha*H + dt * x (outer) B
  *   y [B,H,P] (io_dtype) = H_new . C + D * x
  * y must not overlap the state or any input.  Supported: N in {16, 32, 64,
- * 128, 256}, any P >= 1, io_dtype SSD_F32 or SSD_BF16.
+ * 128, 256}, 1 <= P <= 2^24, io_dtype SSD_F32 or SSD_BF16.
  */
 ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const float *dt, const float *A,
                            const void *B, const void *C, const float *D, float *state, void *y,

@@ -301,7 +301,7 @@ SSD_EXPORT ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const
     if (st != SSD_OK)
         return st;
     const int64_t N = dims->dstate;
-    if (N != 16 && N != 32 && N != 64 && N != 128 && N != 256)
+    if ((N != 16 && N != 32 && N != 64 && N != 128 && N != 256) || dims->headdim > (1 << 24))
         return SSD_ERR_UNSUPPORTED;
     if (dims->batch == 0)
         return SSD_OK;
