@@ -247,6 +247,28 @@ def bench_decode(args):
         out[b] = {"steps": steps, "ms_per_step": wall * 1e3 / steps, "event_ms_per_step": ev_ms,
                   "steps_per_s": steps / wall, "bytes_per_step": nb,
                   "gbs": nb / (ev_ms * 1e-3) / 1e9, "frac": nb / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS}
+        # the same steps captured into one HIP graph and replayed (no per-step
+        # host launch); the state keeps advancing, which costs the same
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for k in range(steps):
+                    ssd.ssd_decode_step(x[k], dt[k], dA, B[k], C[k], dD, state, y=y[k])
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gwall = time.perf_counter() - t0
+        g_ms = e0.elapsed_time(e1) / steps
+        out[b].update({"graph_ms_per_step": gwall * 1e3 / steps, "graph_steps_per_s": steps / gwall,
+                       "graph_gbs": nb / (g_ms * 1e-3) / 1e9})
+        del graph
         del x, dt, B, C, y, state
         torch.cuda.empty_cache()
     return w, out
@@ -388,7 +410,8 @@ def main():
                          "avg_launch_ms": d["event_ms_per_step"]},
             "batches": {str(b): {k: v for k, v in r.items()} for b, r in sorted(dec.items())},
             "note": "batch <= 64 keeps the state (<= 168 MB) in the 256 MB MALL or is "
-                    "launch-bound: effective bandwidth, not HBM",
+                    "launch-bound: effective bandwidth, not HBM; graph_*: the same steps "
+                    "replayed from one captured HIP graph",
         }
         if not args.no_cpu_baseline:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(wd)

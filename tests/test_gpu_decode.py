@@ -101,3 +101,38 @@ def test_decode_step_time_independent_of_context():
         torch.cuda.synchronize()
         times.append(e0.elapsed_time(e1))
     assert max(times) < 3 * min(times)
+
+
+@pytest.mark.parametrize("batch", [1, 256])
+def test_decode_graph_replay(batch):
+    """A run of decode steps captured into one HIP graph (per-step launches
+    replaced by a replay) gives bit-identical y and state to the eager run, on
+    every replay, with eager work and synchronisation between the replays
+    (256: the non-temporal path; 1: the cache-resident one)."""
+    w = si.WORKLOADS["decode_2p7b"]
+    steps = 12
+    state0 = si.random_state(w, batch)
+    _, _, _, y_ref, s_ref = run_decode(w, batch, steps, state0)
+    tok = si.decode_tokens(w, batch, 0, steps)
+    A, D = si.head_params(w)
+    x, dt, B, C = dev(tok["x"], "bf16"), dev(tok["dt"]), dev(tok["B"], "bf16"), dev(tok["C"], "bf16")
+    dA, dD = dev(A), dev(D)
+    s0 = dev(state0.copy())
+    state = s0.clone()
+    ys = torch.empty((steps,) + tuple(x.shape[1:]), dtype=x.dtype, device="cuda")
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            for k in range(steps):
+                ssd.ssd_decode_step(x[k], dt[k], dA, B[k], C[k], dD, state, y=ys[k])
+    torch.cuda.current_stream().wait_stream(side)
+    for rep in range(3):
+        state.copy_(s0)                         # eager reset between replays
+        ys.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(host(ys), y_ref), f"replay {rep}: y"
+        assert np.array_equal(host(state), s_ref), f"replay {rep}: state"
