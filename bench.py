@@ -14,7 +14,7 @@ step is launch-bound).
 Prints ONE JSON line.  ``roofline`` is the dominant prefill kernel
 (chunk_scan_kernel): algorithmic bytes of the layer per launch / its average
 launch time measured with HIP events on the launch stream; ``decode.roofline``
-likewise for decode_kernel.  ``traffic`` comes from committed rocprofv3
+likewise for decode_rows_kernel.  ``traffic`` comes from committed rocprofv3
 FETCH_SIZE / WRITE_SIZE counters (profiles/traffic.json) when they were taken
 on the current kernel sources, else null.  ``cpu_baseline`` times the fp64
 oracle (as it stands) on a bounded sample of the same workload.
@@ -106,10 +106,11 @@ def _counter_means(path, counter):
         if name.startswith(COPY_KERNEL):
             copy += v
         short = name.split("(")[0].split("::")[-1]
-        for k in ("seg_state_kernel", "seg_pass_kernel", "chunk_scan_kernel",
+        for k in ("seg_state_kernel", "chunk_scan_kernel", "decode_rows_kernel",
                   "decode_kernel", "scan_f32_kernel"):
             if k in short or k in name:
                 per.setdefault(k, []).append(v)
+                break
     return {k: sum(v) / len(v) for k, v in per.items()}, copy
 
 
@@ -403,9 +404,9 @@ def main():
             "workload": f"decode_step at the 2.7B shape, state [{main_b},80,64,128] fp32, "
                         f"{d['steps']} consecutive in-place steps, fresh bf16 tokens",
             "steps_per_s": d["steps_per_s"], "ms_per_step": d["ms_per_step"],
-            "roofline": {"bound": "hbm", "kernel": "decode_kernel", "achieved": d["gbs"],
+            "roofline": {"bound": "hbm", "kernel": "decode_rows_kernel", "achieved": d["gbs"],
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
-                         "traffic": committed_traffic("decode_kernel"),
+                         "traffic": committed_traffic("decode_rows_kernel"),
                          "bytes_per_launch": d["bytes_per_step"],
                          "avg_launch_ms": d["event_ms_per_step"]},
             "batches": {str(b): {k: v for k, v in r.items()} for b, r in sorted(dec.items())},
