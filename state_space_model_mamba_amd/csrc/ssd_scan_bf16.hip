@@ -71,9 +71,18 @@ typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kP = 64, kN = 128, kT = 64;     // headdim, dstate, tile tokens
-constexpr int kHeads = 4;                     // heads per work-group
-constexpr int kWaves = 2 * kHeads;            // two waves (P halves) per head
-constexpr int kThreads = 64 * kWaves;
+// Heads per work-group (two waves, one per P half, per head): the scan kernel
+// shares its B/C tiles and C B^T blocks over four heads; the state kernel,
+// which needs neither C nor the blocks, runs one head per work-group so that
+// three fit on a CU.
+constexpr int kScanHeads = 4;
+constexpr int kStateHeads = 1;
+template <int kH> struct Geom {
+    static constexpr int kHeads = kH;
+    static constexpr int kWaves = 2 * kH;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int kBPer = kT * 16 / kThreads;  // 16-byte B (and C) chunks per thread
+};
 // LDS row pitches (bytes).  C is read only row-major (8 bytes at n = 32 kk +
 // 4 g per lane, rows 16 tb + c): a 16-byte pad spreads that over all banks.
 // B is read both row-major and by transpose reads, which no single pitch
@@ -86,8 +95,9 @@ constexpr int kXRow = kP * 2;                 // x tile [s][p], swizzled
 constexpr int kGBlocks = 10;                  // causal 16 x 16 blocks of a 64-token tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <bool kOut> struct ScanSmem;
-template <> struct __align__(16) ScanSmem<true> {
+template <bool kOut, int kH> struct ScanSmem;
+template <int kH> struct __align__(16) ScanSmem<true, kH> {
+    static constexpr int kHeads = kH, kWaves = 2 * kH;
     unsigned char Bt[2][kT * kBRow];          // B[s][n], ring of two tiles
     unsigned char Ct[2][kT * kCRow];          // C[t][n]
     unsigned char Xt[2][kHeads][kT * kXRow];  // x[s][p] of each head
@@ -97,7 +107,8 @@ template <> struct __align__(16) ScanSmem<true> {
     float vt[kWaves][kT];                     // exp(Lam_q - Lam_s) dt_s, q = last token of s's 16-block
     float wd[kWaves][kT];                     // dt_s 2^(bias - log2(e) Lam_s), see stage_tile
 };
-template <> struct __align__(16) ScanSmem<false> {
+template <int kH> struct __align__(16) ScanSmem<false, kH> {
+    static constexpr int kHeads = kH, kWaves = 2 * kH;
     unsigned char Bt[2][kT * kBRow];
     unsigned char Xt[2][kHeads][kT * kXRow];
     float wd[kWaves][kT];
@@ -266,9 +277,9 @@ __device__ __forceinline__ bf16x8 n_operand(const unsigned char *tile, int pitch
 // tid + 512 r of the [64][16 x 16 B] tile); x by the two waves of its head
 // (chunk pt + 128 r of the [64][8 x 16 B] tile, pt = thread within the pair);
 // dt by every wave, lane = token.
-template <bool kOut> struct Prefetch {
-    uint4 b[2];
-    uint4 c[kOut ? 2 : 1];
+template <bool kOut, int kH> struct Prefetch {
+    uint4 b[Geom<kH>::kBPer];
+    uint4 c[kOut ? Geom<kH>::kBPer : 1];
     uint4 x[4];
     float dt;
 };
@@ -313,10 +324,11 @@ __device__ __forceinline__ int64_t tile_bytes(int64_t rows, int64_t pitch, int64
 // with no branches, so the compiler's wait-count analysis sees exactly which
 // loads are outstanding and a prefetched tile stays in flight while the
 // current one is computed.  kPart: 1 = B, C and dt; 2 = x; 3 = all of them.
-template <bool kOut, int kPart = 3>
-__device__ __forceinline__ void load_tile(Prefetch<kOut> &pf, const WaveIo &io, int64_t t0,
+template <bool kOut, int kH, int kPart = 3>
+__device__ __forceinline__ void load_tile(Prefetch<kOut, kH> &pf, const WaveIo &io, int64_t t0,
                                           int64_t L, int tid)
 {
+    constexpr int kPer = Geom<kH>::kBPer, kRows = Geom<kH>::kThreads / 16;
     const int l = tid & 63, pt = tid & 127;
     const int64_t rows = std::min<int64_t>(L - t0, kT);
     const int64_t tb0 = (t0 < L) ? t0 : 0;                   // a valid base when nothing is read
@@ -324,15 +336,15 @@ __device__ __forceinline__ void load_tile(Prefetch<kOut> &pf, const WaveIo &io, 
         const int64_t bp = io.bstride * 2;
         const rsrc_t rb = make_rsrc(io.B + tb0 * io.bstride, tile_bytes(rows, bp, kN * 2));
 #pragma unroll
-        for (int r = 0; r < 2; ++r) {
-            const unsigned off = (unsigned)((tid >> 4) + 32 * r) * (unsigned)bp + (tid & 15) * 16u;
+        for (int r = 0; r < kPer; ++r) {
+            const unsigned off = (unsigned)((tid >> 4) + kRows * r) * (unsigned)bp + (tid & 15) * 16u;
             pf.b[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
         }
         if constexpr (kOut) {
             const rsrc_t rc = make_rsrc(io.C + tb0 * io.bstride, tile_bytes(rows, bp, kN * 2));
 #pragma unroll
-            for (int r = 0; r < 2; ++r) {
-                const unsigned off = (unsigned)((tid >> 4) + 32 * r) * (unsigned)bp + (tid & 15) * 16u;
+            for (int r = 0; r < kPer; ++r) {
+                const unsigned off = (unsigned)((tid >> 4) + kRows * r) * (unsigned)bp + (tid & 15) * 16u;
                 pf.c[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
             }
         }
@@ -384,16 +396,17 @@ struct TileMode {
 // a_t = dt_t A_h over its 64 tokens (lane = token), in log2 units.  Updates ls
 // (and lsum, the segment's total log2 decay) and returns how the tile treats
 // the state.
-template <bool kOut>
-__device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut> &sm, Prefetch<kOut> &pf, int slot,
-                                               int64_t t0, int64_t L, float Ah2, float &ls,
-                                               float &lsum, int tid)
+template <bool kOut, int kH>
+__device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut, kH> &sm, Prefetch<kOut, kH> &pf,
+                                               int slot, int64_t t0, int64_t L, float Ah2,
+                                               float &ls, float &lsum, int tid)
 {
+    constexpr int kPer = Geom<kH>::kBPer, kRows = Geom<kH>::kThreads / 16;
     const int w = wave_id(), l = tid & 63, pt = tid & 127;
     // (rows past the end were loaded as zeros)
 #pragma unroll
-    for (int r = 0; r < 2; ++r) {
-        const int row = (tid >> 4) + 32 * r, col = tid & 15;
+    for (int r = 0; r < kPer; ++r) {
+        const int row = (tid >> 4) + kRows * r, col = tid & 15;
         *reinterpret_cast<uint4 *>(sm.Bt[slot] + row * kBRow + ((col ^ bswz(row)) << 4)) = pf.b[r];
         if constexpr (kOut)
             *reinterpret_cast<uint4 *>(sm.Ct[slot] + row * kCRow + col * 16) = pf.c[r];
@@ -444,9 +457,10 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut> &sm, Prefetch<kOut
 
 // kOut = false: the state kernel (segment end state from zero, to the workspace).
 // kOut = true : the scan kernel (y and, for the last segment, the final state).
-template <bool kOut>
-__device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
+template <bool kOut, int kH>
+__device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &sm)
 {
+    constexpr int kHeads = kH, kWaves = 2 * kH;
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     const int hs = w >> 1;                                // head slot in the work-group
     const int ph = w & 1;                                 // P half: p = 32 ph .. 32 ph + 31
@@ -597,7 +611,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
     };
 
     // y of the tile at t0 from the state entering it, then the state update.
-    Prefetch<kOut> pf;
+    Prefetch<kOut, kH> pf;
     auto compute_tile = [&](int slot, const TileMode &md, int64_t t0) {
         const unsigned char *Xs = sm.Xt[slot][hs];
         const unsigned char *Bs = sm.Bt[slot];
@@ -623,7 +637,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
             }
             // x of the next tile goes out now, so that its registers are not
             // live across the C B^T blocks.
-            load_tile<kOut, 2>(pf, io, t0 + kT, L, tid);
+            load_tile<kOut, kH, 2>(pf, io, t0 + kT, L, tid);
             // Y^T[p][t] = 2^ls exp(Lam_t) sum_n Z[p][n] C[t][n]   (A = Z straight from the accumulators)
             f32x4 Y[2][4];
 #pragma unroll
@@ -735,8 +749,8 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
     // computed.  The barrier at the top of an iteration publishes the slot
     // written at the end of the previous one and guarantees every wave is done
     // reading the slot the current iteration will overwrite.
-    load_tile<kOut>(pf, io, tseg0, L, tid);
-    TileMode mnext = stage_tile<kOut>(sm, pf, 0, tseg0, L, Ah2, ls, lsum, tid);
+    load_tile<kOut, kH>(pf, io, tseg0, L, tid);
+    TileMode mnext = stage_tile<kOut, kH>(sm, pf, 0, tseg0, L, Ah2, ls, lsum, tid);
     int slot = 0;
     for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
         lds_barrier();
@@ -749,11 +763,11 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
                     Z[nb][q] *= md.rscale;
         }
         // next tile (nothing past the end); the scan kernel issues its x loads mid-tile
-        load_tile<kOut, kOut ? 1 : 3>(pf, io, t0 + kT, L, tid);
+        load_tile<kOut, kH, kOut ? 1 : 3>(pf, io, t0 + kT, L, tid);
         compute_tile(slot, md, t0);
         slot ^= 1;
         if (t0 + kT < tseg1)
-            mnext = stage_tile<kOut>(sm, pf, slot, t0 + kT, L, Ah2, ls, lsum, tid);
+            mnext = stage_tile<kOut, kH>(sm, pf, slot, t0 + kT, L, Ah2, ls, lsum, tid);
     }
 
     if (!active)
@@ -779,17 +793,19 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut> &sm)
 }
 
 // State kernel: end state of segments 0 .. nseg-2 from a zero start.
-__global__ __launch_bounds__(kThreads, 1) void seg_state_kernel(SegArgs a)
+// (at most 256 VGPRs: two waves per SIMD, so up to eight of its waves share a CU)
+__global__ __launch_bounds__(Geom<kStateHeads>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
+void seg_state_kernel(SegArgs a)
 {
-    __shared__ ScanSmem<false> sm;
-    seg_body<false>(a, sm);
+    __shared__ ScanSmem<false, kStateHeads> sm;
+    seg_body<false, kStateHeads>(a, sm);
 }
 
 // Scan kernel: y of every segment from its entering state, and the final state.
-__global__ __launch_bounds__(kThreads, 1) void chunk_scan_kernel(SegArgs a)
+__global__ __launch_bounds__(Geom<kScanHeads>::kThreads, 1) void chunk_scan_kernel(SegArgs a)
 {
-    __shared__ ScanSmem<true> sm;
-    seg_body<true>(a, sm);
+    __shared__ ScanSmem<true, kScanHeads> sm;
+    seg_body<true, kScanHeads>(a, sm);
 }
 
 int64_t env_int(const char *name, int64_t dflt)
@@ -815,12 +831,15 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
     Bf16Plan p{};
     p.nchunks = (L + Q - 1) / Q;
     const int64_t hg = G > 0 ? H / G : 1;
-    p.quads = std::max<int64_t>(1, G * ((hg + kHeads - 1) / kHeads));
-    const int64_t per_seg = std::max<int64_t>(1, B * p.quads);     // work-groups per segment
-    // Segments per sequence.  Both kernels run one work-group per CU, so the scan
-    // kernel's time is ~ rounds * chunks per segment; the state kernel (about
-    // half the work per tile) re-reads x for all but the last segment, and
-    // every segment adds state traffic through the workspace.
+    p.quads = std::max<int64_t>(1, G * ((hg + kScanHeads - 1) / kScanHeads));
+    const int64_t per_seg = std::max<int64_t>(1, B * p.quads);     // scan work-groups per segment
+    // state work-groups per segment, and how many fit on the chip at once (LDS)
+    const int64_t per_seg1 = std::max<int64_t>(1, B * G * ((hg + kStateHeads - 1) / kStateHeads));
+    const int64_t slots1 = kCUs * (int64_t)(160 * 1024 / sizeof(ScanSmem<false, kStateHeads>));
+    // Segments per sequence.  The scan kernel runs one work-group per CU, so its
+    // time is ~ rounds * chunks per segment; the state kernel (about half the
+    // work per tile) re-reads x for all but the last segment, and every segment
+    // adds state traffic through the workspace.
     int64_t nseg = env_int("SSD_NSEG", 0);
     if (nseg <= 0) {
         double best = 1e300;
@@ -830,7 +849,7 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
             if (ns != k)
                 continue;
             const double r3 = (double)((per_seg * ns + kCUs - 1) / kCUs);
-            const double r1 = (double)((per_seg * (ns - 1) + kCUs - 1) / kCUs);
+            const double r1 = (double)((per_seg1 * (ns - 1) + slots1 - 1) / slots1);
             const double cost = (r3 + 0.5 * r1) * (double)cps + 0.5 * (double)ns;
             if (cost < best) {
                 best = cost;
@@ -856,7 +875,7 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
             const int64_t nk = (seg_tiles + ut - 1) / ut;           // non-empty units
             if (nk != k)
                 continue;
-            const double rounds = (double)((per_seg * (p.nseg - 1) * nk + kCUs - 1) / kCUs);
+            const double rounds = (double)((per_seg1 * (p.nseg - 1) * nk + slots1 - 1) / slots1);
             // (a chained state costs the scan kernel's critical path ~ 3 tiles)
             const double cost = rounds * (double)ut + (double)nk + 3.0 * (double)((p.nseg - 1) * nk);
             if (want > 0 ? k == want : cost < best) {
@@ -894,7 +913,8 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     a.H = (int)H;
     a.G = (int)G;
     a.hg = (int)(H / G);
-    a.nq = (int)((a.hg + kHeads - 1) / kHeads);
+    const int nq3 = (a.hg + kScanHeads - 1) / kScanHeads;
+    const int nq1 = (a.hg + kStateHeads - 1) / kStateHeads;
     a.seg_tokens = plan.chunks_per_seg * Q;
     a.unit_tokens = plan.unit_tokens;
     a.nseg = (int)plan.nseg;
@@ -905,18 +925,19 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     char *wsb = static_cast<char *>(ws);
     a.ws_state = reinterpret_cast<float *>(wsb);
     a.ws_decay = reinterpret_cast<float *>(wsb + align256(plan.state_bytes));
-    const int64_t per_seg = B * G * a.nq;
     hipError_t e = log_begin(log, s);
     if (e != hipSuccess)
         return e;
     if (plan.nseg > 1) {
+        a.nq = nq1;
         a.nseg_launch = (a.nseg - 1) * a.nsub;
-        seg_state_kernel<<<(unsigned)(per_seg * a.nseg_launch), kThreads, 0, s>>>(a);
+        seg_state_kernel<<<(unsigned)(B * G * nq1 * a.nseg_launch), Geom<kStateHeads>::kThreads, 0, s>>>(a);
         if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "seg_state_kernel", s)) != hipSuccess)
             return e;
     }
+    a.nq = nq3;
     a.nseg_launch = a.nseg;
-    chunk_scan_kernel<<<(unsigned)(per_seg * plan.nseg), kThreads, 0, s>>>(a);
+    chunk_scan_kernel<<<(unsigned)(B * G * nq3 * plan.nseg), Geom<kScanHeads>::kThreads, 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return log_kernel(log, "chunk_scan_kernel", s);
