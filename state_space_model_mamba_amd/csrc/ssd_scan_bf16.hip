@@ -419,7 +419,11 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut, kH> &sm, Prefetch<
     }
     const float dtl = pf.dt;
     const float lam = wave_inclusive_sum(dtl * Ah2, l);
-    const float lam_end = lane_f(lam, 63);
+    // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
+    // hold the same sum only up to the summation order, which matters when
+    // the decay is extreme and Lam is large)
+    const int last = (int)((L - t0 < kT) ? (L - t0) : kT) - 1;
+    const float lam_end = lane_f(lam, last);
     lsum += lam_end;
     TileMode md;
     md.renorm = false;

@@ -251,3 +251,48 @@ def test_timed_entry_point_matches():
     y2, s2, times = ssd.ssd_chunk_scan_timed(g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], 256)
     assert torch.equal(y1, y2) and torch.equal(s1, s2)
     assert [n for n, _ in times][-1] == "chunk_scan_kernel" and all(ms > 0 for _, ms in times)
+
+
+def _scan_with_heads(A, dt_scale, seed, L=1100, h0=True):
+    """Scan with chosen per-head A (fp32) and dt scaled by dt_scale, against the
+    oracle on the same (rounded) values."""
+    H = len(A)
+    w = si.small_workload(batch=2, seqlen=L, nheads=H, chunk=128, seed=seed)
+    inp = si.prefill_inputs(w)
+    inp["dt"] = (inp["dt"] * np.float32(dt_scale)).astype(np.float32)
+    A = np.asarray(A, dtype=np.float32)
+    _, D = si.head_params(w)
+    g = dict(x=dev(inp["x"], "bf16"), dt=dev(inp["dt"]), B=dev(inp["B"], "bf16"),
+             C=dev(inp["C"], "bf16"), A=dev(A), D=dev(D))
+    s0 = (np.random.default_rng(seed).standard_normal((2, H, 64, 128)).astype(np.float32)
+          if h0 else None)
+    wid = widen_inputs(inp, "bf16")
+    for Dv in (D, np.zeros_like(D)):
+        y, s = gpu_scan(g, 128, D=dev(Dv), init=None if s0 is None else dev(s0))
+        yref, sref = oracle.ssd_scan(wid["x"], wid["dt"], A.astype(np.float64), wid["B"], wid["C"],
+                                     Dv.astype(np.float64),
+                                     h0=None if s0 is None else s0.astype(np.float64), nthreads=16)
+        assert np.isfinite(host(y)).all() and np.isfinite(host(s)).all()
+        check_y(host(y), yref, TOL["bf16"])
+        if np.abs(sref).max() > 0:
+            check_state(host(s), sref, TOL["bf16"])
+
+
+def test_extreme_decay_memoryless():
+    """A = -1e6: every tile's decay underflows, so y_t = dt_t (B_t . C_t) x_t + D x_t
+    (the direct-decay path on every tile, and the masked exponents at -inf)."""
+    _scan_with_heads([-1e6, -1e6, -5e5, -1e6], 1.0, seed=31)
+
+
+def test_no_decay():
+    """A = 0: the state is a plain prefix sum that grows along the sequence (the
+    lazy scale never moves)."""
+    _scan_with_heads([0.0, 0.0, 0.0, 0.0], 1.0, seed=32)
+
+
+def test_decay_mix_renormalisation():
+    """Heads from no decay to strong decay with long tiles' worth of tokens, so
+    that the lazily applied state scale is renormalised, applied directly, or
+    left alone, head by head."""
+    _scan_with_heads([0.0, -0.05, -1.0, -16.0, -100.0, -3.0, -0.5, -40.0], 1.0, seed=33, L=2300)
+    _scan_with_heads([-16.0, -8.0, -4.0, -1.0], 10.0, seed=34, L=700)
