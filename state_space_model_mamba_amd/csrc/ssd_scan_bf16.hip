@@ -83,8 +83,9 @@ template <int kH> struct Geom {
     static constexpr int kThreads = 64 * kWaves;
     static constexpr int kBPer = kT * 16 / kThreads;  // 16-byte B (and C) chunks per thread
 };
-// LDS row pitches (bytes).  C is read only row-major (8 bytes at n = 32 kk +
-// 4 g per lane, rows 16 tb + c): a 16-byte pad spreads that over all banks.
+// LDS row pitches (bytes).  C is read only row-major (16 bytes per lane from
+// rows 16 tb + c, after the permutation below): a 16-byte pad spreads the 16
+// rows of a lane group over all banks.
 // B is read both row-major and by transpose reads, which no single pitch
 // serves, so its rows are unpadded and their 16-byte chunks are permuted by an
 // XOR with bswz(row), which makes both patterns conflict-free; x (transpose
@@ -260,6 +261,24 @@ __device__ __forceinline__ bf16x8 n_operand_b(const unsigned char *tile, int row
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// The C tile is stored with each 32-element block of n permuted so that the
+// operand's K-slots (n = 32 kk + 16 h + 4 g + i at slot 4 h + i of lane group
+// g) are 8 contiguous elements: n_local = 16 h + 4 g + i sits at 8 g + 4 h + i.
+// Staging: the 16-byte chunk `col` (n = 8 col .. +7, m = col % 4 within its
+// block) splits into two 8-byte halves (g = 2 (m % 2) and g + 1, h = m / 2).
+__device__ __forceinline__ void cstage(unsigned char *row, int col, uint4 v)
+{
+    const int m = col & 3;
+    const int p0 = (col & ~3) * 8 + 16 * (m & 1) + 4 * (m >> 1);   // element position
+    *reinterpret_cast<uint2 *>(row + p0 * 2) = make_uint2(v.x, v.y);
+    *reinterpret_cast<uint2 *>(row + (p0 + 8) * 2) = make_uint2(v.z, v.w);
+}
+// The operand from the permuted C tile: one 16-byte read.
+__device__ __forceinline__ bf16x8 c_operand(const unsigned char *tile, int row, int kk, int g)
+{
+    return *reinterpret_cast<const bf16x8 *>(tile + row * kCRow + (32 * kk + 8 * g) * 2);
+}
+
 // Row-major MFMA operand over n from a [row][n] LDS tile.  K-slot 4 h + i of
 // lane group g is n = 32 kk + 16 h + 4 g + i -- the map under which the state
 // accumulators (rows n = 16 nb + 4 g + i) are directly an operand.
@@ -409,7 +428,7 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut, kH> &sm, Prefetch<
         const int row = (tid >> 4) + kRows * r, col = tid & 15;
         *reinterpret_cast<uint4 *>(sm.Bt[slot] + row * kBRow + ((col ^ bswz(row)) << 4)) = pf.b[r];
         if constexpr (kOut)
-            *reinterpret_cast<uint4 *>(sm.Ct[slot] + row * kCRow + col * 16) = pf.c[r];
+            cstage(sm.Ct[slot] + row * kCRow, col, pf.c[r]);
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
@@ -635,7 +654,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
 #pragma unroll
                     for (int kk = 0; kk < 4; ++kk)
                         gacc = mfma32(n_operand_b(Bs, 16 * sb + c, kk, g),
-                                      n_operand(Cs, kCRow, 16 * tb + c, kk, g), gacc);
+                                      c_operand(Cs, 16 * tb + c, kk, g), gacc);
                     sm.Gs[bi][l] = gacc;
                 }
             }
@@ -649,7 +668,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
                 bf16x8 CF[4];
 #pragma unroll
                 for (int tb = 0; tb < 4; ++tb)
-                    CF[tb] = n_operand(Cs, kCRow, 16 * tb + c, kk, g);
+                    CF[tb] = c_operand(Cs, 16 * tb + c, kk, g);
 #pragma unroll
                 for (int q = 0; q < 2; ++q) {
                     bf16x8 za;
