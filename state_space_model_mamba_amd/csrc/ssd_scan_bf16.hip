@@ -522,11 +522,12 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
     io.B = a.B + (b * L * a.G + grp) * kN;
     io.C = a.C + (b * L * a.G + grp) * kN;
     io.dt = a.dt + b * L * a.H + h;
-    // y of lane (c, g) in token block tb: row 16 tb + c, columns 16 (2 ph + q) + 4 g .. +3;
-    // byte offsets from the tile's first row (a tile spans 64 rows of H * P elements)
+    // y as stored: lane (c, g) of token block tb writes row 16 tb + c, columns
+    // 32 ph + 8 g .. +7; byte offsets from the tile's first row (a tile spans 64
+    // rows of H * P elements)
     const int64_t ystride = (int64_t)a.H * kP;
     __bf16 *ybase = kOut ? a.y + (b * L * a.H + h) * kP : nullptr;
-    const unsigned ylane = ((unsigned)c * (unsigned)ystride + 32u * ph + 4u * g) * 2u;
+    const unsigned ylane = ((unsigned)c * (unsigned)ystride + 32u * ph + 8u * g) * 2u;
 
     // State accumulators: Z[nb][q][i] = R[p = 32 ph + 16 q + c][n = 16 nb + 4 g + i] / 2^ls.
     const int zoff = (32 * ph + c) * kN + 4 * g;      // + 16 q kN + 16 nb
@@ -740,22 +741,35 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
                     if (tb >= 2)
                         Y[q][tb] = mfma32(XT[q][1], MOP[tb][1], Y[q][tb]);
                 }
-            if (active) {
-                // rows past the end fall outside the descriptor and are dropped
-                const rsrc_t ry = make_rsrc(ybase + t0 * ystride,
-                                            tile_bytes(std::min<int64_t>(L - t0, kT), ystride * 2, kP * 2));
+            // Lane (c, g) holds columns 16 q + 4 g .. +3 (q = 0, 1) of the wave's
+            // half of row 16 tb + c.  Swapping the upper and lower 32 lanes of the
+            // q = 1 and q = 0 registers, then the odd and even 16-lane rows, leaves
+            // lane (c, g) with columns 8 g .. 8 g + 7 in (r0, r1), so one store
+            // writes 16 rows x 64 contiguous bytes.  Rows past the end fall
+            // outside the descriptor and are dropped, and an idle wave's
+            // descriptor is empty.  The stores are issued on every path: under a
+            // branch, the wait for the next tile's loads in stage_tile would also
+            // wait for these stores to complete.
+            const rsrc_t ry = make_rsrc(ybase + t0 * ystride,
+                                        active ? tile_bytes(std::min<int64_t>(L - t0, kT), ystride * 2, kP * 2) : 0);
 #pragma unroll
-                for (int tb = 0; tb < 4; ++tb)
+            for (int tb = 0; tb < 4; ++tb) {
+                bf16x4 y0, y1;
 #pragma unroll
-                    for (int q = 0; q < 2; ++q) {
-                        bf16x4 yv;
+                for (int i = 0; i < 4; ++i) {
+                    y0[i] = (__bf16)Y[0][tb][i];
+                    y1[i] = (__bf16)Y[1][tb][i];
+                }
+                u32x2 r0 = __builtin_bit_cast(u32x2, y0), r1 = __builtin_bit_cast(u32x2, y1);
 #pragma unroll
-                        for (int i = 0; i < 4; ++i)
-                            yv[i] = (__bf16)Y[q][tb][i];
-                        __builtin_amdgcn_raw_buffer_store_b64(
-                            __builtin_bit_cast(u32x2, yv), ry,
-                            ylane + 32u * tb * (unsigned)ystride + 32u * q, 0, 0);
-                    }
+                for (int d = 0; d < 2; ++d) {
+                    const u32x2 s32 = __builtin_amdgcn_permlane32_swap(r0[d], r1[d], false, false);
+                    const u32x2 s16 = __builtin_amdgcn_permlane16_swap(s32[0], s32[1], false, false);
+                    r0[d] = s16[0];
+                    r1[d] = s16[1];
+                }
+                const u32x4 v = {r0[0], r0[1], r1[0], r1[1]};
+                __builtin_amdgcn_raw_buffer_store_b128(v, ry, ylane + 32u * tb * (unsigned)ystride, 0, 0);
             }
         } else {
 #pragma unroll
