@@ -39,13 +39,14 @@
 // * The next tile's global loads are issued before the current tile is
 //   computed and land in registers (software pipelining).
 // * Sequence parallelism: a (b, h) sequence is cut into segments of whole
-//   chunks.  The state kernel computes each segment's end state from a zero
-//   start (segments 0 .. nseg-2); the scan kernel chains those into the state
-//   entering its own segment (S_in[k+1] = decay_k S_in[k] + S_loc[k]) and
-//   re-walks the segment from it, writing y (and the final state).  The
-//   segment count is chosen so that the scan kernel fills the chip in as few
-//   rounds as possible while every extra segment costs one more pass of its
-//   x through HBM.
+//   chunks, and segments 0 .. nseg-2 into units.  The state kernel computes
+//   each unit's end state from a zero start, with its B and x tiles loaded
+//   straight into a three-slot LDS ring two tiles ahead; the scan kernel
+//   chains those into the state entering its own segment (S_in[k+1] =
+//   decay_k S_in[k] + S_loc[k]) and re-walks the segment from it, writing y
+//   (and the final state).  The segment count is chosen so that the scan
+//   kernel fills the chip in as few rounds as possible while every extra
+//   segment costs one more pass of its x through HBM.
 // * Work-groups are remapped so that neighbouring (batch row, segment, head
 //   quad) work lands on one XCD and shares its L2 for the B/C tiles.
 //
@@ -71,12 +72,9 @@ typedef short s16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
 
 constexpr int kP = 64, kN = 128, kT = 64;     // headdim, dstate, tile tokens
-// Heads per work-group (two waves, one per P half, per head): the scan kernel
-// shares its B/C tiles and C B^T blocks over four heads; the state kernel,
-// which needs neither C nor the blocks, runs one head per work-group so that
-// three fit on a CU.
+// Heads per scan work-group (two waves, one per P half, per head), which
+// share its B/C tiles and C B^T blocks.
 constexpr int kScanHeads = 4;
-constexpr int kStateHeads = 1;
 template <int kH> struct Geom {
     static constexpr int kHeads = kH;
     static constexpr int kWaves = 2 * kH;
@@ -96,8 +94,7 @@ constexpr int kXRow = kP * 2;                 // x tile [s][p], swizzled
 constexpr int kGBlocks = 10;                  // causal 16 x 16 blocks of a 64-token tile
 constexpr float kLog2e = 1.4426950408889634f;
 
-template <bool kOut, int kH> struct ScanSmem;
-template <int kH> struct __align__(16) ScanSmem<true, kH> {
+template <int kH> struct __align__(16) ScanSmem {
     static constexpr int kHeads = kH, kWaves = 2 * kH;
     unsigned char Bt[2][kT * kBRow];          // B[s][n], ring of two tiles
     unsigned char Ct[2][kT * kCRow];          // C[t][n]
@@ -108,13 +105,6 @@ template <int kH> struct __align__(16) ScanSmem<true, kH> {
     float vt[kWaves][kT];                     // exp(Lam_q - Lam_s) dt_s, q = last token of s's 16-block
     float wd[kWaves][kT];                     // dt_s 2^(bias - log2(e) Lam_s), see stage_tile
 };
-template <int kH> struct __align__(16) ScanSmem<false, kH> {
-    static constexpr int kHeads = kH, kWaves = 2 * kH;
-    unsigned char Bt[2][kT * kBRow];
-    unsigned char Xt[2][kHeads][kT * kXRow];
-    float wd[kWaves][kT];
-};
-
 struct SegArgs {
     const __bf16 *x;
     const float *dt;
@@ -296,9 +286,9 @@ __device__ __forceinline__ bf16x8 n_operand(const unsigned char *tile, int pitch
 // tid + 512 r of the [64][16 x 16 B] tile); x by the two waves of its head
 // (chunk pt + 128 r of the [64][8 x 16 B] tile, pt = thread within the pair);
 // dt by every wave, lane = token.
-template <bool kOut, int kH> struct Prefetch {
+template <int kH> struct Prefetch {
     uint4 b[Geom<kH>::kBPer];
-    uint4 c[kOut ? Geom<kH>::kBPer : 1];
+    uint4 c[Geom<kH>::kBPer];
     uint4 x[4];
     float dt;
 };
@@ -321,20 +311,20 @@ typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
-// Buffer resource over [base, base + bytes) (raw, 32-bit data: the gfx9-family
-// descriptor word).  Buffer loads past `bytes` return zero and stores there are
-// dropped, so one descriptor per tile, ending after the last valid row, both
-// bounds and zero-fills a ragged tile without any per-lane arithmetic.
-__device__ __forceinline__ rsrc_t make_rsrc(const void *base, int64_t bytes)
+// Buffer resource (raw, 32-bit data: the gfx9-family descriptor word) over
+// the rows of a tile starting at `base` of which min(rows, kT) are valid
+// (none if rows <= 0).  Buffer loads past its end return zero and stores
+// there are dropped, so one resource per tile both bounds and zero-fills a
+// ragged tile without per-lane arithmetic.  It is computed without branches:
+// a select around the loads would make the compiler duplicate them and lose
+// track of which are in flight.  A tile spans at most kT rows, so its byte
+// count is 32-bit.
+__device__ __forceinline__ rsrc_t tile_rsrc(const void *base, int64_t rows, unsigned pitch,
+                                            unsigned row_bytes)
 {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0,
-                                             (int)(bytes > 0 ? bytes : 0), 0x00020000);
-}
-
-// Bytes from a tile's first row to the end of its last valid row.
-__device__ __forceinline__ int64_t tile_bytes(int64_t rows, int64_t pitch, int64_t row_bytes)
-{
-    return rows > 0 ? (rows - 1) * pitch + row_bytes : 0;
+    const int r = (int)std::max<int64_t>(0, std::min<int64_t>(rows, kT));
+    const int bytes = std::max(r * (int)pitch - (int)pitch + (int)row_bytes, 0);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
 // Issue the global loads of the tile starting at t0, through buffer resources
@@ -343,40 +333,37 @@ __device__ __forceinline__ int64_t tile_bytes(int64_t rows, int64_t pitch, int64
 // with no branches, so the compiler's wait-count analysis sees exactly which
 // loads are outstanding and a prefetched tile stays in flight while the
 // current one is computed.  kPart: 1 = B, C and dt; 2 = x; 3 = all of them.
-template <bool kOut, int kH, int kPart = 3>
-__device__ __forceinline__ void load_tile(Prefetch<kOut, kH> &pf, const WaveIo &io, int64_t t0,
+template <int kH, int kPart = 3>
+__device__ __forceinline__ void load_tile(Prefetch<kH> &pf, const WaveIo &io, int64_t t0,
                                           int64_t L, int tid)
 {
     constexpr int kPer = Geom<kH>::kBPer, kRows = Geom<kH>::kThreads / 16;
     const int l = tid & 63, pt = tid & 127;
-    const int64_t rows = std::min<int64_t>(L - t0, kT);
-    const int64_t tb0 = (t0 < L) ? t0 : 0;                   // a valid base when nothing is read
+    const int64_t rows = L - t0;
     if constexpr ((kPart & 1) != 0) {
-        const int64_t bp = io.bstride * 2;
-        const rsrc_t rb = make_rsrc(io.B + tb0 * io.bstride, tile_bytes(rows, bp, kN * 2));
+        const unsigned bp = (unsigned)io.bstride * 2u;
+        const rsrc_t rb = tile_rsrc(io.B + t0 * io.bstride, rows, bp, kN * 2);
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
-            const unsigned off = (unsigned)((tid >> 4) + kRows * r) * (unsigned)bp + (tid & 15) * 16u;
+            const unsigned off = (unsigned)((tid >> 4) + kRows * r) * bp + (tid & 15) * 16u;
             pf.b[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rb, off, 0, 0));
         }
-        if constexpr (kOut) {
-            const rsrc_t rc = make_rsrc(io.C + tb0 * io.bstride, tile_bytes(rows, bp, kN * 2));
+        const rsrc_t rc = tile_rsrc(io.C + t0 * io.bstride, rows, bp, kN * 2);
 #pragma unroll
-            for (int r = 0; r < kPer; ++r) {
-                const unsigned off = (unsigned)((tid >> 4) + kRows * r) * (unsigned)bp + (tid & 15) * 16u;
-                pf.c[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
-            }
+        for (int r = 0; r < kPer; ++r) {
+            const unsigned off = (unsigned)((tid >> 4) + kRows * r) * bp + (tid & 15) * 16u;
+            pf.c[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
         }
-        const int64_t dp = (int64_t)io.dtstride * 4;
-        const rsrc_t rd = make_rsrc(io.dt + tb0 * io.dtstride, tile_bytes(rows, dp, 4));
-        pf.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (unsigned)l * (unsigned)dp, 0, 0));
+        const unsigned dp = (unsigned)io.dtstride * 4u;
+        const rsrc_t rd = tile_rsrc(io.dt + t0 * io.dtstride, rows, dp, 4);
+        pf.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (unsigned)l * dp, 0, 0));
     }
     if constexpr ((kPart & 2) != 0) {
-        const int64_t xp = io.xstride * 2;
-        const rsrc_t rx = make_rsrc(io.x + tb0 * io.xstride, tile_bytes(rows, xp, kP * 2));
+        const unsigned xp = (unsigned)io.xstride * 2u;
+        const rsrc_t rx = tile_rsrc(io.x + t0 * io.xstride, rows, xp, kP * 2);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const unsigned off = (unsigned)((pt >> 3) + 16 * r) * (unsigned)xp + (pt & 7) * 16u;
+            const unsigned off = (unsigned)((pt >> 3) + 16 * r) * xp + (pt & 7) * 16u;
             pf.x[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0));
         }
     }
@@ -411,43 +398,15 @@ struct TileMode {
     float rscale;
 };
 
-// Registers -> LDS for one tile, and the tile's decay tables: each wave scans
-// a_t = dt_t A_h over its 64 tokens (lane = token), in log2 units.  Updates ls
-// (and lsum, the segment's total log2 decay) and returns how the tile treats
-// the state.
-template <bool kOut, int kH>
-__device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut, kH> &sm, Prefetch<kOut, kH> &pf,
-                                               int slot, int64_t t0, int64_t L, float Ah2,
-                                               float &ls, float &lsum, int tid)
+// How a tile with total log2 decay lam_end treats the state R = 2^ls Z (see
+// kRenorm); updates ls and lsum (the unit's total log2 decay).  The tile's
+// update weights are wd_s = dt_s 2^(bias - lam_s).
+__device__ __forceinline__ TileMode tile_mode(float lam_end, float &ls, float &lsum, float &bias)
 {
-    constexpr int kPer = Geom<kH>::kBPer, kRows = Geom<kH>::kThreads / 16;
-    const int w = wave_id(), l = tid & 63, pt = tid & 127;
-    // (rows past the end were loaded as zeros)
-#pragma unroll
-    for (int r = 0; r < kPer; ++r) {
-        const int row = (tid >> 4) + kRows * r, col = tid & 15;
-        *reinterpret_cast<uint4 *>(sm.Bt[slot] + row * kBRow + ((col ^ bswz(row)) << 4)) = pf.b[r];
-        if constexpr (kOut)
-            cstage(sm.Ct[slot] + row * kCRow, col, pf.c[r]);
-    }
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int row = (pt >> 3) + 16 * r;
-        *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow +
-                                   (((pt & 7) ^ xswz(row)) << 4)) = pf.x[r];
-    }
-    const float dtl = pf.dt;
-    const float lam = wave_inclusive_sum(dtl * Ah2, l);
-    // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
-    // hold the same sum only up to the summation order, which matters when
-    // the decay is extreme and Lam is large)
-    const int last = (int)((L - t0 < kT) ? (L - t0) : kT) - 1;
-    const float lam_end = lane_f(lam, last);
     lsum += lam_end;
     TileMode md;
     md.renorm = false;
     md.rscale = 1.f;
-    float bias;                                   // wd_s = dt_s 2^(bias - lam_s)
     if (lam_end < -kRenorm) {
         md.direct = true;
         md.ly = ls;
@@ -466,22 +425,106 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kOut, kH> &sm, Prefetch<
         bias = -ls;
         ls += lam_end;
     }
-    sm.wd[w][l] = fast_exp2(bias - lam) * dtl;
-    if constexpr (kOut) {
-        const float q0 = lane_f(lam, 15), q1 = lane_f(lam, 31), q2 = lane_f(lam, 47);
-        const int row = l >> 4;
-        const float lq = row == 0 ? q0 : row == 1 ? q1 : row == 2 ? q2 : lam_end;
-        sm.lam[w][l] = lam;
-        sm.dtv[w][l] = dtl;
-        sm.vt[w][l] = fast_exp2(lq - lam) * dtl;
-    }
     return md;
 }
 
-// kOut = false: the state kernel (segment end state from zero, to the workspace).
-// kOut = true : the scan kernel (y and, for the last segment, the final state).
-template <bool kOut, int kH>
-__device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &sm)
+// Z <- zscale Z + B^T (wd x) over one tile, with Z[nb][q][i] the state rows
+// n = 16 nb + 4 g + i, column p = 32 ph + 16 q + c (lane (c, g)) of this
+// wave's P half.  A = B^T (rows n) from the swizzled B tile, B = x^T scaled by
+// the tile's weights wd (64 floats, token-indexed).  The B^T operands are read
+// kAhead blocks ahead of their MFMAs, so that their LDS latency overlaps the
+// x scaling and the previous blocks' MFMAs.
+template <int kAhead>
+__device__ __forceinline__ void state_update(f32x4 (&Z)[8][2], const unsigned char *Bs,
+                                             const bf16x8 (&XT)[2][2], const float *wd,
+                                             const TileMode &md, int g, int c)
+{
+    bf16x8 BT[8][2];
+#pragma unroll
+    for (int nb = 0; nb < kAhead; ++nb) {
+        BT[nb][0] = tr_operand_b(Bs, 0, 16 * nb, g, c);
+        BT[nb][1] = tr_operand_b(Bs, 1, 16 * nb, g, c);
+    }
+    f32x4 wv[2][2];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+            wv[jj][hh] = *reinterpret_cast<const f32x4 *>(&wd[32 * jj + 16 * hh + 4 * g]);
+    bf16x8 XS[2][2];
+#pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                XS[q][jj][e] = (__bf16)((float)XT[q][jj][e] * wv[jj][e >> 2][e & 3]);
+    if (uniform(md.direct)) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                Z[nb][q] *= md.zscale;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+        if (nb + kAhead < 8) {
+            BT[nb + kAhead][0] = tr_operand_b(Bs, 0, 16 * (nb + kAhead), g, c);
+            BT[nb + kAhead][1] = tr_operand_b(Bs, 1, 16 * (nb + kAhead), g, c);
+        }
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            Z[nb][q] = mfma32(BT[nb][1], XS[q][1], mfma32(BT[nb][0], XS[q][0], Z[nb][q]));
+    }
+}
+
+// Registers -> LDS for one tile, and the tile's decay tables: each wave scans
+// a_t = dt_t A_h over its 64 tokens (lane = token), in log2 units.  Updates ls
+// (and lsum, the segment's total log2 decay) and returns how the tile treats
+// the state.
+template <int kH>
+__device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &pf,
+                                               int slot, int64_t t0, int64_t L, float Ah2,
+                                               float &ls, float &lsum, int tid)
+{
+    constexpr int kPer = Geom<kH>::kBPer, kRows = Geom<kH>::kThreads / 16;
+    const int w = wave_id(), l = tid & 63, pt = tid & 127;
+    // (rows past the end were loaded as zeros)
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int row = (tid >> 4) + kRows * r, col = tid & 15;
+        *reinterpret_cast<uint4 *>(sm.Bt[slot] + row * kBRow + ((col ^ bswz(row)) << 4)) = pf.b[r];
+        cstage(sm.Ct[slot] + row * kCRow, col, pf.c[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int row = (pt >> 3) + 16 * r;
+        *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow +
+                                   (((pt & 7) ^ xswz(row)) << 4)) = pf.x[r];
+    }
+    const float dtl = pf.dt;
+    const float lam = wave_inclusive_sum(dtl * Ah2, l);
+    // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
+    // hold the same sum only up to the summation order, which matters when
+    // the decay is extreme and Lam is large)
+    const int last = (int)((L - t0 < kT) ? (L - t0 > 0 ? L - t0 : 1) : kT) - 1;
+    const float lam_end = lane_f(lam, last);
+    float bias;
+    const TileMode md = tile_mode(lam_end, ls, lsum, bias);
+    sm.wd[w][l] = fast_exp2(bias - lam) * dtl;
+    const float q0 = lane_f(lam, 15), q1 = lane_f(lam, 31), q2 = lane_f(lam, 47);
+    const int row = l >> 4;
+    const float lq = row == 0 ? q0 : row == 1 ? q1 : row == 2 ? q2 : lam_end;
+    sm.lam[w][l] = lam;
+    sm.dtv[w][l] = dtl;
+    sm.vt[w][l] = fast_exp2(lq - lam) * dtl;
+    return md;
+}
+
+// The scan kernel: y of segment `seg` from the state entering it and, for the
+// last segment, the final state.
+template <int kH>
+__device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
 {
     constexpr int kHeads = kH, kWaves = 2 * kH;
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
@@ -499,19 +542,10 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
     const int h = grp * a.hg + (active ? hw : a.hg - 1);
     const int64_t bh = b * a.H + h;
     const int64_t L = a.L;
-    // The scan kernel walks segment `seg`; the state kernel walks unit `seg`
-    // (part `seg % nsub` of segment `seg / nsub`).
-    int64_t tseg0, tseg1;
-    if (kOut) {
-        tseg0 = (int64_t)seg * a.seg_tokens;
-        tseg1 = std::min<int64_t>(L, tseg0 + a.seg_tokens);
-    } else {
-        const int64_t sbeg = (int64_t)(seg / a.nsub) * a.seg_tokens;
-        tseg0 = sbeg + (int64_t)(seg % a.nsub) * a.unit_tokens;
-        tseg1 = std::min<int64_t>(std::min<int64_t>(L, sbeg + a.seg_tokens), tseg0 + a.unit_tokens);
-    }
+    const int64_t tseg0 = (int64_t)seg * a.seg_tokens;
+    const int64_t tseg1 = std::min<int64_t>(L, tseg0 + a.seg_tokens);
     const float Ah2 = a.A[h] * kLog2e;
-    const float Dh = kOut ? a.D[h] : 0.f;
+    const float Dh = a.D[h];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
     WaveIo io;
@@ -526,15 +560,15 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
     // 32 ph + 8 g .. +7; byte offsets from the tile's first row (a tile spans 64
     // rows of H * P elements)
     const int64_t ystride = (int64_t)a.H * kP;
-    __bf16 *ybase = kOut ? a.y + (b * L * a.H + h) * kP : nullptr;
+    __bf16 *ybase = a.y + (b * L * a.H + h) * kP;
     const unsigned ylane = ((unsigned)c * (unsigned)ystride + 32u * ph + 8u * g) * 2u;
 
     // State accumulators: Z[nb][q][i] = R[p = 32 ph + 16 q + c][n = 16 nb + 4 g + i] / 2^ls.
     const int zoff = (32 * ph + c) * kN + 4 * g;      // + 16 q kN + 16 nb
     f32x4 Z[8][2];
     {
-        // Scan kernel: the state entering the segment, from the initial state
-        // and the end states S_k of the earlier units (state kernel), i.e. the
+        // The state entering the segment, from the initial state and the end
+        // states S_k of the earlier units (state kernel), i.e. the
         // chain S <- d_k S + S_k written out as
         //   S_in = (prod_k d_k) S_init + sum_k (prod_{j > k} d_j) S_k,
         // summed from the last unit backwards so that the loads of all units
@@ -542,29 +576,25 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
         // When the final state aliases the initial state, the state kernel has
         // copied the initial state to the spare slot.
         const float *src = nullptr;
-        if (kOut) {
-            if (a.seg0_from_ws)
-                src = a.ws_state + (bh * a.nslot + (a.nslot - 1)) * kP * kN;
-            else if (a.init)
-                src = a.init + bh * kP * kN;
-        }
+        if (a.seg0_from_ws)
+            src = a.ws_state + (bh * a.nslot + (a.nslot - 1)) * kP * kN;
+        else if (a.init)
+            src = a.init + bh * kP * kN;
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
             for (int q = 0; q < 2; ++q)
                 Z[nb][q] = zero4;
         float wgt = 1.f;                              // prod_{j > k} d_j
-        if (kOut) {
 #pragma unroll 2
-            for (int k = seg * a.nsub - 1; k >= 0; --k) {
-                const float *sl = a.ws_state + (bh * a.nslot + k) * kP * kN;
+        for (int k = seg * a.nsub - 1; k >= 0; --k) {
+            const float *sl = a.ws_state + (bh * a.nslot + k) * kP * kN;
 #pragma unroll
-                for (int nb = 0; nb < 8; ++nb)
+            for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-                    for (int q = 0; q < 2; ++q)
-                        Z[nb][q] += *reinterpret_cast<const f32x4 *>(sl + zoff + 16 * q * kN + 16 * nb) * wgt;
-                wgt *= a.ws_decay[bh * a.nslot + k];
-            }
+                for (int q = 0; q < 2; ++q)
+                    Z[nb][q] += *reinterpret_cast<const f32x4 *>(sl + zoff + 16 * q * kN + 16 * nb) * wgt;
+            wgt *= a.ws_decay[bh * a.nslot + k];
         }
         if (src) {
 #pragma unroll
@@ -573,74 +603,23 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
                 for (int q = 0; q < 2; ++q)
                     Z[nb][q] += *reinterpret_cast<const f32x4 *>(src + zoff + 16 * q * kN + 16 * nb) * wgt;
         }
-        if (!kOut && seg == 0 && a.seg0_from_ws && active) {
-            // alias of final and initial state: keep a copy of the initial state
-            const float *ini = a.init + bh * kP * kN;
-            float *cp = a.ws_state + (bh * a.nslot + (a.nslot - 1)) * kP * kN;
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    *reinterpret_cast<f32x4 *>(cp + zoff + 16 * q * kN + 16 * nb) =
-                        *reinterpret_cast<const f32x4 *>(ini + zoff + 16 * q * kN + 16 * nb);
-        }
     }
     float ls = 0.f;         // R = 2^ls Z
     float lsum = 0.f;       // log2 of the product of tile decays over the segment
 
-    // R <- zscale R + B^T (w dt x):  A = B^T (rows n), B = scaled x (columns p)
+    // R <- zscale R + B^T (w dt x); in the scan kernel the prefetched tile is
+    // live here, so the B^T operands are read half a tile ahead
     auto update_state = [&](const unsigned char *Bs, const bf16x8 (&XT)[2][2], const TileMode &md) {
-        // B^T operands are read ahead of their MFMAs (all of them in the state
-        // kernel; in the scan kernel, whose prefetched tile is live here, half at
-        // a time), so that
-        // their LDS latency overlaps the x scaling and the previous half's MFMAs.
-        constexpr int kAhead = kOut ? 4 : 8;
-        bf16x8 BT[8][2];
-#pragma unroll
-        for (int nb = 0; nb < kAhead; ++nb) {
-            BT[nb][0] = tr_operand_b(Bs, 0, 16 * nb, g, c);
-            BT[nb][1] = tr_operand_b(Bs, 1, 16 * nb, g, c);
-        }
-        f32x4 wv[2][2];
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                wv[jj][hh] = *reinterpret_cast<const f32x4 *>(&sm.wd[w][32 * jj + 16 * hh + 4 * g]);
-        bf16x8 XS[2][2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-#pragma unroll
-                for (int e = 0; e < 8; ++e)
-                    XS[q][jj][e] = (__bf16)((float)XT[q][jj][e] * wv[jj][e >> 2][e & 3]);
-        if (uniform(md.direct)) {
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb)
-#pragma unroll
-                for (int q = 0; q < 2; ++q)
-                    Z[nb][q] *= md.zscale;
-        }
-#pragma unroll
-        for (int nb = 0; nb < 8; ++nb) {
-            if (nb + kAhead < 8) {
-                BT[nb + kAhead][0] = tr_operand_b(Bs, 0, 16 * (nb + kAhead), g, c);
-                BT[nb + kAhead][1] = tr_operand_b(Bs, 1, 16 * (nb + kAhead), g, c);
-            }
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-                Z[nb][q] = mfma32(BT[nb][1], XS[q][1], mfma32(BT[nb][0], XS[q][0], Z[nb][q]));
-        }
+        state_update<4>(Z, Bs, XT, sm.wd[w], md, g, c);
     };
 
     // y of the tile at t0 from the state entering it, then the state update.
-    Prefetch<kOut, kH> pf;
+    Prefetch<kH> pf;
     auto compute_tile = [&](int slot, const TileMode &md, int64_t t0) {
         const unsigned char *Xs = sm.Xt[slot][hs];
         const unsigned char *Bs = sm.Bt[slot];
         bf16x8 XT[2][2];      // x^T: rows p (this wave's half), K over tokens
-        if constexpr (kOut) {
+        {
             const unsigned char *Cs = sm.Ct[slot];
             // (C B^T)^T causal blocks, shared by the four heads: wave w computes
             // blocks w and w + 8 of the ten; lane (c, g) of block (sb, tb) holds
@@ -661,7 +640,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
             }
             // x of the next tile goes out now, so that its registers are not
             // live across the C B^T blocks.
-            load_tile<kOut, kH, 2>(pf, io, t0 + kT, L, tid);
+            load_tile<kH, 2>(pf, io, t0 + kT, L, tid);
             // Y^T[p][t] = 2^ls exp(Lam_t) sum_n Z[p][n] C[t][n]   (A = Z straight from the accumulators)
             f32x4 Y[2][4];
 #pragma unroll
@@ -750,8 +729,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
             // descriptor is empty.  The stores are issued on every path: under a
             // branch, the wait for the next tile's loads in stage_tile would also
             // wait for these stores to complete.
-            const rsrc_t ry = make_rsrc(ybase + t0 * ystride,
-                                        active ? tile_bytes(std::min<int64_t>(L - t0, kT), ystride * 2, kP * 2) : 0);
+            const rsrc_t ry = tile_rsrc(ybase + t0 * ystride, active ? L - t0 : 0, (unsigned)ystride * 2u, kP * 2);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 bf16x4 y0, y1;
@@ -771,12 +749,6 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
                 const u32x4 v = {r0[0], r0[1], r1[0], r1[1]};
                 __builtin_amdgcn_raw_buffer_store_b128(v, ry, ylane + 32u * tb * (unsigned)ystride, 0, 0);
             }
-        } else {
-#pragma unroll
-            for (int q = 0; q < 2; ++q)
-#pragma unroll
-                for (int jj = 0; jj < 2; ++jj)
-                    XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
         }
         update_state(Bs, XT, md);
     };
@@ -786,12 +758,7 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
     // computed.  The barrier at the top of an iteration publishes the slot
     // written at the end of the previous one and guarantees every wave is done
     // reading the slot the current iteration will overwrite.
-    load_tile<kOut, kH>(pf, io, tseg0, L, tid);
-    TileMode mnext = stage_tile<kOut, kH>(sm, pf, 0, tseg0, L, Ah2, ls, lsum, tid);
-    int slot = 0;
-    for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
-        lds_barrier();
-        const TileMode md = mnext;
+    auto renorm = [&](const TileMode &md) {
         if (uniform(md.renorm)) {
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb)
@@ -799,26 +766,31 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
                 for (int q = 0; q < 2; ++q)
                     Z[nb][q] *= md.rscale;
         }
-        // next tile (nothing past the end); the scan kernel issues its x loads mid-tile
-        load_tile<kOut, kH, kOut ? 1 : 3>(pf, io, t0 + kT, L, tid);
+    };
+    // Tile k is staged in ring slot k & 1 (B, C, x) and in the wave's own
+    // tables; tile k + 1's loads are in flight in `pf` while tile k is
+    // computed.  The barrier at the top of an iteration publishes the slot
+    // written at the end of the previous one and guarantees every wave is done
+    // reading the slot the current iteration will overwrite.
+    load_tile<kH>(pf, io, tseg0, L, tid);
+    TileMode mnext = stage_tile<kH>(sm, pf, 0, tseg0, L, Ah2, ls, lsum, tid);
+    int slot = 0;
+    for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
+        lds_barrier();
+        const TileMode md = mnext;
+        renorm(md);
+        // next tile (nothing past the end); x follows mid-tile
+        load_tile<kH, 1>(pf, io, t0 + kT, L, tid);
         compute_tile(slot, md, t0);
         slot ^= 1;
         if (t0 + kT < tseg1)
-            mnext = stage_tile<kOut, kH>(sm, pf, slot, t0 + kT, L, Ah2, ls, lsum, tid);
+            mnext = stage_tile<kH>(sm, pf, slot, t0 + kT, L, Ah2, ls, lsum, tid);
     }
 
-    if (!active)
+    if (!active || seg != a.nseg - 1)
         return;
-    float *dst = nullptr;
-    if (kOut) {
-        if (seg == a.nseg - 1)
-            dst = a.fin + bh * kP * kN;
-    } else {
-        dst = a.ws_state + (bh * a.nslot + seg) * kP * kN;
-        if (tid == 128 * hs)
-            a.ws_decay[bh * a.nslot + seg] = fast_exp2(lsum);
-    }
-    if (dst) {
+    {
+        float *dst = a.fin + bh * kP * kN;
         const float sc = fast_exp2(ls);
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
@@ -829,20 +801,244 @@ __device__ __forceinline__ void seg_body(const SegArgs &a, ScanSmem<kOut, kH> &s
     }
 }
 
-// State kernel: end state of segments 0 .. nseg-2 from a zero start.
-// (at most 256 VGPRs: two waves per SIMD, so up to eight of its waves share a CU)
-__global__ __launch_bounds__(Geom<kStateHeads>::kThreads) __attribute__((amdgpu_waves_per_eu(2)))
-void seg_state_kernel(SegArgs a)
+// State kernel: the end state of every unit (part of segments 0 .. nseg-2)
+// from a zero start, and the unit's total decay.  A unit is a plain sequence
+// of tile updates, so what bounds it is how much of HBM's latency its loads
+// can hide: its B and x tiles go straight from memory into a ring of three
+// LDS slots (buffer loads with an LDS destination, no registers in between),
+// two tiles ahead of the one being computed, with one barrier per tile.
+// Four heads per work-group share each B tile; wave w = (head w / 2, P half
+// w % 2) loads half of its own head's x tile.
+constexpr int kStHeads = 4, kStWaves = 2 * kStHeads, kStThreads = 64 * kStWaves;
+constexpr int kStBBlocks = kT * kBRow / 1024 / kStWaves;   // 1 KB B blocks per wave per tile
+constexpr int kStXBlocks = kT * kXRow / 1024 / 2;          // 1 KB x blocks per wave per tile
+constexpr int kStLoads = kStBBlocks + kStXBlocks + 1;      // memory instructions per wave per tile (+ dt)
+constexpr size_t kStSmemBytes = 3 * (size_t)kT * (kBRow + kStHeads * kXRow + kStWaves * 4) + (size_t)kStWaves * kT * 4;
+
+struct StIo {
+    const __bf16 *B, *x;       // this (b, group) / (b, head) at token 0
+    const float *dt;
+    int64_t bp, xp, dp;        // bytes per token
+    unsigned boff[kStBBlocks]; // this lane's source offset within a tile, per block
+    unsigned xoff[kStXBlocks];
+    unsigned doff;
+};
+
+// Buffer resource words over the valid rows of a tile (as tile_rsrc), for
+// the loads below.
+__device__ __forceinline__ u32x4 tile_words(const void *base, int64_t rows, unsigned pitch,
+                                            unsigned row_bytes)
 {
-    __shared__ ScanSmem<false, kStateHeads> sm;
-    seg_body<false, kStateHeads>(a, sm);
+    const int r = (int)std::max<int64_t>(0, std::min<int64_t>(rows, kT));
+    const uint64_t p = reinterpret_cast<uint64_t>(base);
+    u32x4 d;
+    d.x = __builtin_amdgcn_readfirstlane((unsigned)p);
+    d.y = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32)) & 0xffffu;
+    d.z = __builtin_amdgcn_readfirstlane((unsigned)std::max(r * (int)pitch - (int)pitch + (int)row_bytes, 0));
+    d.w = 0x00020000u;
+    return d;
+}
+
+// Buffer loads with an LDS destination: lane l's 16 (4) bytes land at
+// dst + 16 l (4 l).  They are written out here so that the compiler does not
+// insert its own waits for them (it cannot tell the ring slots apart and
+// would wait for every one in flight); their reader waits with wait_vmcnt and
+// a barrier.  Nothing is written to registers.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void lds_load16(unsigned dst, u32x4 rsrc, unsigned voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+                 :: "s"(dst), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+__device__ __forceinline__ void lds_load4(unsigned dst, u32x4 rsrc, unsigned voff)
+{
+    asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dword %1, %2, 0 offen lds"
+                 :: "s"(dst), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// Loads of the tile at t0 into one ring slot, bounded by the unit's end (a
+// tile past it reads as zeros): kStLoads instructions per wave.  Lane l of a
+// 1 KB block writes bytes 16 l .. 16 l + 15 of it, so the swizzle of the B
+// and x tiles is applied to the source offsets.
+__device__ __forceinline__ void st_issue(const StIo &io, unsigned Bslot, unsigned Xslot, unsigned Dslot,
+                                         int64_t t0, int64_t tend, int w)
+{
+    const int64_t rows = tend - t0;
+    const u32x4 rb = tile_words(io.B + t0 * (io.bp / 2), rows, (unsigned)io.bp, kN * 2);
+#pragma unroll
+    for (int k = 0; k < kStBBlocks; ++k)
+        lds_load16(Bslot + 1024 * (kStBBlocks * w + k), rb, io.boff[k]);
+    const u32x4 rx = tile_words(io.x + t0 * (io.xp / 2), rows, (unsigned)io.xp, kP * 2);
+#pragma unroll
+    for (int k = 0; k < kStXBlocks; ++k)
+        lds_load16(Xslot + 1024 * (kStXBlocks * (w & 1) + k), rx, io.xoff[k]);
+    const u32x4 rd = tile_words(io.dt + t0 * (io.dp / 4), rows, (unsigned)io.dp, 4);
+    lds_load4(Dslot, rd, io.doff);
+}
+
+// The LDS location at byte address a, as a pointer.
+__device__ __forceinline__ const unsigned char *lds_ptr(unsigned a)
+{
+    return (const unsigned char *)(const __attribute__((address_space(3))) unsigned char *)(uintptr_t)a;
+}
+
+// s_waitcnt vmcnt(n), other counters untouched (gfx9 encoding)
+template <int n> __device__ __forceinline__ void wait_vmcnt()
+{
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
+}
+
+__global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
+{
+    __shared__ __align__(16) unsigned char sB0[kT * kBRow], sB1[kT * kBRow], sB2[kT * kBRow];
+    __shared__ __align__(16) unsigned char sX0[kStHeads][kT * kXRow], sX1[kStHeads][kT * kXRow],
+        sX2[kStHeads][kT * kXRow];
+    __shared__ __align__(16) unsigned char sD0[kStWaves][kT * 4], sD1[kStWaves][kT * 4], sD2[kStWaves][kT * 4];
+    __shared__ __align__(16) float swd[kStWaves][kT];
+
+    const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
+    const int hs = w >> 1, ph = w & 1;
+    const int64_t j = xcd_remap(blockIdx.x, gridDim.x);
+    const int nquad = a.G * a.nq;
+    const int quad = (int)(j % nquad);
+    const int64_t r = j / nquad;
+    const int unit = (int)(r % a.nseg_launch);
+    const int64_t b = r / a.nseg_launch;
+    const int grp = quad / a.nq;
+    const int hw = (quad % a.nq) * kStHeads + hs;
+    const bool active = hw < a.hg;                        // idle slots mirror the last head
+    const int h = grp * a.hg + (active ? hw : a.hg - 1);
+    const int64_t bh = b * a.H + h;
+    const int64_t L = a.L;
+    const int64_t sbeg = (int64_t)(unit / a.nsub) * a.seg_tokens;
+    const int64_t tseg0 = sbeg + (int64_t)(unit % a.nsub) * a.unit_tokens;
+    const int64_t tseg1 = std::min<int64_t>(std::min<int64_t>(L, sbeg + a.seg_tokens), tseg0 + a.unit_tokens);
+    const float Ah2 = a.A[h] * kLog2e;
+    const int zoff = (32 * ph + c) * kN + 4 * g;          // + 16 q kN + 16 nb
+
+    if (unit == 0 && a.seg0_from_ws && active) {
+        // alias of final and initial state: keep a copy of the initial state
+        const float *ini = a.init + bh * kP * kN;
+        float *cp = a.ws_state + (bh * a.nslot + (a.nslot - 1)) * kP * kN;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                *reinterpret_cast<f32x4 *>(cp + zoff + 16 * q * kN + 16 * nb) =
+                    *reinterpret_cast<const f32x4 *>(ini + zoff + 16 * q * kN + 16 * nb);
+    }
+
+    StIo io;
+    io.bp = (int64_t)a.G * kN * 2;
+    io.xp = (int64_t)a.H * kP * 2;
+    io.dp = (int64_t)a.H * 4;
+    io.B = a.B + (b * L * a.G + grp) * kN;
+    io.x = a.x + (b * L * a.H + h) * kP;
+    io.dt = a.dt + b * L * a.H + h;
+#pragma unroll
+    for (int k = 0; k < kStBBlocks; ++k) {
+        const int row = 4 * (kStBBlocks * w + k) + (l >> 4), pc = l & 15;
+        io.boff[k] = (unsigned)row * (unsigned)io.bp + (unsigned)((pc ^ bswz(row)) << 4);
+    }
+#pragma unroll
+    for (int k = 0; k < kStXBlocks; ++k) {
+        const int row = 8 * (kStXBlocks * ph + k) + (l >> 3), pc = l & 7;
+        io.xoff[k] = (unsigned)row * (unsigned)io.xp + (unsigned)((pc ^ xswz(row)) << 4);
+    }
+    io.doff = (unsigned)l * (unsigned)io.dp;
+
+    // Zero the ring once: rows past a unit's end then hold zeros or an older
+    // tile's finite values, which its zero weights cancel.
+    {
+        uint4 *z0 = reinterpret_cast<uint4 *>(sB0), *z1 = reinterpret_cast<uint4 *>(sB1),
+              *z2 = reinterpret_cast<uint4 *>(sB2);
+        for (int i = tid; i < kT * kBRow / 16; i += kStThreads)
+            z0[i] = z1[i] = z2[i] = make_uint4(0, 0, 0, 0);
+        uint4 *x0 = reinterpret_cast<uint4 *>(&sX0[0][0]), *x1 = reinterpret_cast<uint4 *>(&sX1[0][0]),
+              *x2 = reinterpret_cast<uint4 *>(&sX2[0][0]);
+        for (int i = tid; i < kStHeads * kT * kXRow / 16; i += kStThreads)
+            x0[i] = x1[i] = x2[i] = make_uint4(0, 0, 0, 0);
+    }
+    lds_barrier();
+
+    f32x4 Z[8][2];
+    const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            Z[nb][q] = zero4;
+    float ls = 0.f, lsum = 0.f;
+    // LDS byte addresses of the slots (scalars; the loads take them in M0)
+#define SSD_LDS(p) __builtin_amdgcn_readfirstlane( \
+    (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(p)))
+    const unsigned aB0 = SSD_LDS(sB0), aB1 = SSD_LDS(sB1), aB2 = SSD_LDS(sB2);
+    const unsigned aX0 = SSD_LDS(&sX0[hs][0]), aX1 = SSD_LDS(&sX1[hs][0]), aX2 = SSD_LDS(&sX2[hs][0]);
+    const unsigned aD0 = SSD_LDS(&sD0[w][0]), aD1 = SSD_LDS(&sD1[w][0]), aD2 = SSD_LDS(&sD2[w][0]);
+#undef SSD_LDS
+    st_issue(io, aB0, aX0, aD0, tseg0, tseg1, w);
+    st_issue(io, aB1, aX1, aD1, tseg0 + kT, tseg1, w);
+
+    // tile t0 in slot (Bs, Xs, Ds); tile t0 + 2 kT goes to (Bn, Xn, Dn)
+    auto step = [&](unsigned aB, unsigned aX, unsigned aD, unsigned Bn, unsigned Xn, unsigned Dn,
+                    int64_t t0) {
+        wait_vmcnt<kStLoads>();                   // this wave's loads of tile t0 are in
+        lds_barrier();                            // ... and every wave's; slot of t0 - kT free
+        st_issue(io, Bn, Xn, Dn, t0 + 2 * kT, tseg1, w);
+        const unsigned char *Bs = lds_ptr(aB), *Xs = lds_ptr(aX), *Ds = lds_ptr(aD);
+        const float dtc = reinterpret_cast<const float *>(Ds)[l];
+        const float lam = wave_inclusive_sum(dtc * Ah2, l);
+        const int last = (int)std::min<int64_t>(std::max<int64_t>(tseg1 - t0, 1), kT) - 1;
+        float bias;
+        const TileMode md = tile_mode(lane_f(lam, last), ls, lsum, bias);
+        if (uniform(md.renorm)) {
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+                for (int q = 0; q < 2; ++q)
+                    Z[nb][q] *= md.rscale;
+        }
+        swd[w][l] = fast_exp2(bias - lam) * dtc;
+        bf16x8 XT[2][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
+        state_update<8>(Z, Bs, XT, swd[w], md, g, c);
+    };
+    // the ring's slots: c = tile t0, m = tile t0 + kT (in flight), f = free
+    unsigned cB = aB0, cX = aX0, cD = aD0, mB = aB1, mX = aX1, mD = aD1, fB = aB2, fX = aX2, fD = aD2;
+    for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
+        step(cB, cX, cD, fB, fX, fD, t0);
+        const unsigned oB = cB, oX = cX, oD = cD;
+        cB = mB, cX = mX, cD = mD;
+        mB = fB, mX = fX, mD = fD;
+        fB = oB, fX = oX, fD = oD;
+    }
+    wait_vmcnt<0>();   // the loads past the end land before the work-group's LDS is released
+
+    if (!active)
+        return;
+    float *dst = a.ws_state + (bh * a.nslot + unit) * kP * kN;
+    if (tid == 128 * hs)
+        a.ws_decay[bh * a.nslot + unit] = fast_exp2(lsum);
+    const float sc = fast_exp2(ls);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            *reinterpret_cast<f32x4 *>(dst + zoff + 16 * q * kN + 16 * nb) = Z[nb][q] * sc;
 }
 
 // Scan kernel: y of every segment from its entering state, and the final state.
 __global__ __launch_bounds__(Geom<kScanHeads>::kThreads, 1) void chunk_scan_kernel(SegArgs a)
 {
-    __shared__ ScanSmem<true, kScanHeads> sm;
-    seg_body<true, kScanHeads>(a, sm);
+    __shared__ ScanSmem<kScanHeads> sm;
+    scan_body<kScanHeads>(a, sm);
 }
 
 int64_t env_int(const char *name, int64_t dflt)
@@ -871,8 +1067,8 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
     p.quads = std::max<int64_t>(1, G * ((hg + kScanHeads - 1) / kScanHeads));
     const int64_t per_seg = std::max<int64_t>(1, B * p.quads);     // scan work-groups per segment
     // state work-groups per segment, and how many fit on the chip at once (LDS)
-    const int64_t per_seg1 = std::max<int64_t>(1, B * G * ((hg + kStateHeads - 1) / kStateHeads));
-    const int64_t slots1 = kCUs * (int64_t)(160 * 1024 / sizeof(ScanSmem<false, kStateHeads>));
+    const int64_t per_seg1 = std::max<int64_t>(1, B * G * ((hg + kStHeads - 1) / kStHeads));
+    const int64_t slots1 = kCUs * (int64_t)(160 * 1024 / kStSmemBytes);
     // Segments per sequence.  The scan kernel runs one work-group per CU, so its
     // time is ~ rounds * chunks per segment; the state kernel (about half the
     // work per tile) re-reads x for all but the last segment, and every segment
@@ -913,8 +1109,8 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
             if (nk != k)
                 continue;
             const double rounds = (double)((per_seg1 * (p.nseg - 1) * nk + slots1 - 1) / slots1);
-            // (a chained state costs the scan kernel's critical path ~ 3 tiles)
-            const double cost = rounds * (double)ut + (double)nk + 3.0 * (double)((p.nseg - 1) * nk);
+            // (a chained state costs the scan kernel's critical path ~ 1 tile)
+            const double cost = rounds * (double)ut + (double)nk + (double)((p.nseg - 1) * nk);
             if (want > 0 ? k == want : cost < best) {
                 best = cost;
                 p.nsub = nk;
@@ -951,7 +1147,7 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     a.G = (int)G;
     a.hg = (int)(H / G);
     const int nq3 = (a.hg + kScanHeads - 1) / kScanHeads;
-    const int nq1 = (a.hg + kStateHeads - 1) / kStateHeads;
+    const int nq1 = (a.hg + kStHeads - 1) / kStHeads;
     a.seg_tokens = plan.chunks_per_seg * Q;
     a.unit_tokens = plan.unit_tokens;
     a.nseg = (int)plan.nseg;
@@ -968,7 +1164,7 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     if (plan.nseg > 1) {
         a.nq = nq1;
         a.nseg_launch = (a.nseg - 1) * a.nsub;
-        seg_state_kernel<<<(unsigned)(B * G * nq1 * a.nseg_launch), Geom<kStateHeads>::kThreads, 0, s>>>(a);
+        seg_state_kernel<<<(unsigned)(B * G * nq1 * a.nseg_launch), kStThreads, 0, s>>>(a);
         if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "seg_state_kernel", s)) != hipSuccess)
             return e;
     }
