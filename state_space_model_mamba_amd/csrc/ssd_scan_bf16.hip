@@ -640,7 +640,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
             }
             // x of the next tile goes out now, so that its registers are not
             // live across the C B^T blocks.
-            load_tile<kH, 2>(pf, io, t0 + kT, L, tid);
+            load_tile<kH, 2>(pf, io, t0 + kT, tseg1, tid);
             // Y^T[p][t] = 2^ls exp(Lam_t) sum_n Z[p][n] C[t][n]   (A = Z straight from the accumulators)
             f32x4 Y[2][4];
 #pragma unroll
@@ -771,20 +771,22 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
     // tables; tile k + 1's loads are in flight in `pf` while tile k is
     // computed.  The barrier at the top of an iteration publishes the slot
     // written at the end of the previous one and guarantees every wave is done
-    // reading the slot the current iteration will overwrite.
-    load_tile<kH>(pf, io, tseg0, L, tid);
-    TileMode mnext = stage_tile<kH>(sm, pf, 0, tseg0, L, Ah2, ls, lsum, tid);
+    // reading the slot the current iteration will overwrite.  Loads end at
+    // the segment's last token: the tile after it reads as zeros, and staging
+    // it leaves ls unchanged, so every iteration stages without a branch
+    // (which lets the compiler interleave the staging with the update).
+    load_tile<kH>(pf, io, tseg0, tseg1, tid);
+    TileMode mnext = stage_tile<kH>(sm, pf, 0, tseg0, tseg1, Ah2, ls, lsum, tid);
     int slot = 0;
     for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
         lds_barrier();
         const TileMode md = mnext;
         renorm(md);
         // next tile (nothing past the end); x follows mid-tile
-        load_tile<kH, 1>(pf, io, t0 + kT, L, tid);
+        load_tile<kH, 1>(pf, io, t0 + kT, tseg1, tid);
         compute_tile(slot, md, t0);
         slot ^= 1;
-        if (t0 + kT < tseg1)
-            mnext = stage_tile<kH>(sm, pf, slot, t0 + kT, L, Ah2, ls, lsum, tid);
+        mnext = stage_tile<kH>(sm, pf, slot, t0 + kT, tseg1, Ah2, ls, lsum, tid);
     }
 
     if (!active || seg != a.nseg - 1)
