@@ -300,13 +300,6 @@ struct WaveIo {
     int dtstride;
 };
 
-// Issue the global loads of the tile starting at t0.  Always the same
-// instructions with no branches around them (rows past the end are clamped
-// to the last valid token and zeroed in stage_tile), so the compiler's
-// wait-count analysis sees exactly which loads are outstanding and a
-// prefetched tile stays in flight while the current one is computed.  t0 may
-// lie past the end of the segment: the caller then never stages that tile.
-// Offsets are 32-bit (a tile spans at most 64 rows of H*P or G*N elements).
 typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -328,11 +321,13 @@ __device__ __forceinline__ rsrc_t tile_rsrc(const void *base, int64_t rows, unsi
 }
 
 // Issue the global loads of the tile starting at t0, through buffer resources
-// that end at the last valid token, so a ragged tile reads zeros and a tile
-// past the end of the sequence reads nothing.  Always the same instructions
-// with no branches, so the compiler's wait-count analysis sees exactly which
-// loads are outstanding and a prefetched tile stays in flight while the
-// current one is computed.  kPart: 1 = B, C and dt; 2 = x; 3 = all of them.
+// that end at token L (the caller passes the segment's end), so a ragged tile
+// reads zeros and a tile past the end reads nothing.  Always the same
+// instructions with no branches, so the compiler's wait-count analysis sees
+// exactly which loads are outstanding and a prefetched tile stays in flight
+// while the current one is computed.  Offsets are 32-bit (a tile spans at
+// most 64 rows of H*P or G*N elements).  kPart: 1 = B, C and dt; 2 = x; 3 =
+// all of them.
 template <int kH, int kPart = 3>
 __device__ __forceinline__ void load_tile(Prefetch<kH> &pf, const WaveIo &io, int64_t t0,
                                           int64_t L, int tid)
@@ -607,8 +602,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
     float ls = 0.f;         // R = 2^ls Z
     float lsum = 0.f;       // log2 of the product of tile decays over the segment
 
-    // R <- zscale R + B^T (w dt x); in the scan kernel the prefetched tile is
-    // live here, so the B^T operands are read half a tile ahead
+    // R <- zscale R + B^T (w dt x); the prefetched tile is live here, so the
+    // B^T operands are read half a tile ahead
     auto update_state = [&](const unsigned char *Bs, const bf16x8 (&XT)[2][2], const TileMode &md) {
         state_update<4>(Z, Bs, XT, sm.wd[w], md, g, c);
     };
