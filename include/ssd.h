@@ -102,7 +102,9 @@ ssd_status ssd_state_init(const ssd_dims *dims, float *state, const float *src, 
 /*
  * ssd_chunk_scan_workspace_size -- bytes of device workspace ssd_chunk_scan
  * needs for these sizes (0 is possible).  *bytes is written on SSD_OK.  The
- * result depends on dims only.
+ * result depends on dims only (and on the environment variables SSD_NSEG /
+ * SSD_NSUB, which override the planner's segment and unit counts when set
+ * to a positive integer; the tests use them).
  */
 ssd_status ssd_chunk_scan_workspace_size(const ssd_dims *dims, size_t *bytes);
 
