@@ -148,6 +148,29 @@ ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const float *dt,
                            void *stream);
 
 /*
+ * ssd_decode_steps -- nsteps consecutive cached decode steps in one launch:
+ * the same result as calling ssd_decode_step nsteps times, step k on the k-th
+ * slice of each input, but the state is read once, kept on-chip (in
+ * registers) across all steps and written once (section 2 of the page: the
+ * decode loop runs on the device around the state cache; "A Persistent-State
+ * Dataflow Accelerator for Memory-Bound Linear Attention Decode on FPGA",
+ * section 2A: a state that persists on-chip across steps is not re-read
+ * from external memory).  The tokens of all steps must be known in advance
+ * (teacher-forced steps, appending a short known segment to a cache).
+ *   x [S,B,H,P], dt [S,B,H], A [H], B [S,B,G,N], C [S,B,G,N], D [H]   inputs, S = nsteps
+ *   state [B,H,P,N] fp32, updated in place (H after step S)
+ *   y [S,B,H,P] (io_dtype), y[k] = output of step k
+ * Step-major layout: slice k of x, dt, B, C, y is exactly what one
+ * ssd_decode_step call takes.  nsteps == 0 or B == 0 does nothing; nsteps < 0
+ * is SSD_ERR_SHAPE.  y must not overlap the state or any input; the state
+ * must not overlap an input.  Supported: N in {16, 32, 64, 128, 256},
+ * 1 <= P <= 2^24, io_dtype SSD_F32 or SSD_BF16, nsteps <= INT32_MAX.
+ */
+ssd_status ssd_decode_steps(const ssd_dims *dims, int64_t nsteps, const void *x, const float *dt,
+                            const float *A, const void *B, const void *C, const float *D,
+                            float *state, void *y, void *stream);
+
+/*
  * ssd_chunk_scan_timed -- measurement entry point: the same computation as
  * ssd_chunk_scan (same arguments and results), run synchronously; the device
  * time of each kernel the scan launched is written to kernel_ms[0 ..

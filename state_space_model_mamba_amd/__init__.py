@@ -11,6 +11,7 @@ Functions keep the C names:
     ssd_chunk_scan_workspace_size(...)
     ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, ...) -> (y, final_state)
     ssd_decode_step(x, dt, A, B, C, D, state, y=None) -> y
+    ssd_decode_steps(x, dt, A, B, C, D, state, y=None) -> y   (S steps in one launch)
     ssd_chunk_scan_timed(...) -> (y, final_state, [(kernel, ms), ...])
 """
 from __future__ import annotations
@@ -25,7 +26,7 @@ SSD_F32, SSD_BF16 = 0, 1
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_ALIAS", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_DEVICE", 7: "SSD_ERR_ALIGNMENT"}
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_state_init", "ssd_chunk_scan_workspace_size",
-           "ssd_chunk_scan", "ssd_decode_step", "ssd_chunk_scan_timed")
+           "ssd_chunk_scan", "ssd_decode_step", "ssd_decode_steps", "ssd_chunk_scan_timed")
 
 
 class SsdError(RuntimeError):
@@ -74,6 +75,8 @@ def load(path: str | None = None):
     lib.ssd_chunk_scan_timed.restype = ctypes.c_int
     lib.ssd_decode_step.argtypes = [dims] + [vp] * 9
     lib.ssd_decode_step.restype = ctypes.c_int
+    lib.ssd_decode_steps.argtypes = [dims, ctypes.c_int64] + [vp] * 9
+    lib.ssd_decode_steps.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -177,4 +180,19 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
     _check("ssd_decode_step", load().ssd_decode_step(
         ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
         _ptr(y), _stream(stream)))
+    return y
+
+
+def ssd_decode_steps(x, dt, A, B, C, D, state, y=None, stream=None):
+    """S decode steps in one launch: x[S, B, H, P], dt[S, B, H], B/C[S, B, G, N];
+    state[B, H, P, N] updated in place (read and written once); returns y[S, B, H, P]."""
+    import torch
+    nsteps, bsz, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x))
+    if y is None:
+        y = torch.empty_like(x)
+    _check("ssd_decode_steps", load().ssd_decode_steps(
+        ctypes.byref(d), ctypes.c_int64(nsteps), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+        _ptr(D), _ptr(state), _ptr(y), _stream(stream)))
     return y

@@ -323,3 +323,46 @@ SSD_EXPORT ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const
     return device_status(ssd::launch_decode(dims->io_dtype == SSD_BF16, Bn, H, P, N, G, x, dt, A,
                                             B, C, D, state, y, static_cast<hipStream_t>(stream)));
 }
+
+SSD_EXPORT ssd_status ssd_decode_steps(const ssd_dims *dims, int64_t nsteps, const void *x,
+                                       const float *dt, const float *A, const void *B,
+                                       const void *C, const float *D, float *state, void *y,
+                                       void *stream)
+{
+    ssd_status st = check_dims(dims, false);
+    if (st != SSD_OK)
+        return st;
+    if (nsteps < 0)
+        return SSD_ERR_SHAPE;
+    const int64_t N = dims->dstate;
+    if ((N != 16 && N != 32 && N != 64 && N != 128 && N != 256) || dims->headdim > (1 << 24))
+        return SSD_ERR_UNSUPPORTED;
+    const int64_t Bn = dims->batch, H = dims->nheads, P = dims->headdim, G = dims->ngroups;
+    // the kernel indexes steps and waves (at most one per two state rows) in 32 bits
+    if (nsteps > INT32_MAX || Bn * H * ((P + 1) / 2) > INT32_MAX - 4)
+        return SSD_ERR_UNSUPPORTED;
+    if (Bn == 0 || nsteps == 0)
+        return SSD_OK;
+    if (!x || !dt || !A || !B || !C || !D || !state || !y)
+        return SSD_ERR_NULL;
+    const int64_t esz = dims->io_dtype == SSD_BF16 ? 2 : 4;
+    int64_t xbytes, bbytes, dbytes;
+    if (!mul_ok(nsteps, Bn * H * P, &xbytes) || !mul_ok(xbytes, esz, &xbytes) ||
+        !mul_ok(nsteps, Bn * G * N, &bbytes) || !mul_ok(bbytes, esz, &bbytes) ||
+        !mul_ok(nsteps, Bn * H, &dbytes) || !mul_ok(dbytes, 4, &dbytes))
+        return SSD_ERR_SHAPE;
+    if (!aligned(state, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(x, esz) ||
+        !aligned(y, esz) || !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4))
+        return SSD_ERR_ALIGNMENT;
+    const Span ss = span(state, Bn * H * P * N * 4), sy = span(y, xbytes);
+    const Span ins[] = {span(x, xbytes), span(dt, dbytes), span(A, H * 4), span(B, bbytes),
+                        span(C, bbytes), span(D, H * 4)};
+    for (const Span &in : ins)
+        if (overlap(sy, in) || overlap(ss, in))
+            return SSD_ERR_ALIAS;
+    if (overlap(sy, ss))
+        return SSD_ERR_ALIAS;
+    return device_status(ssd::launch_decode_steps(dims->io_dtype == SSD_BF16, nsteps, Bn, H, P,
+                                                  N, G, x, dt, A, B, C, D, state, y,
+                                                  static_cast<hipStream_t>(stream)));
+}

@@ -29,6 +29,13 @@ hipError_t launch_decode(int bf16, int64_t B, int64_t H, int64_t P, int64_t N, i
                          const void *x, const float *dt, const float *A, const void *Bm,
                          const void *Cm, const float *D, float *state, void *y, hipStream_t s);
 
+// S consecutive decode steps in one launch (state kept in registers across
+// them); x, y [S, B, H, P], dt [S, B, H], B/C [S, B, G, N].
+hipError_t launch_decode_steps(int bf16, int64_t S, int64_t B, int64_t H, int64_t P, int64_t N,
+                               int64_t G, const void *x, const float *dt, const float *A,
+                               const void *Bm, const void *Cm, const float *D, float *state,
+                               void *y, hipStream_t s);
+
 // fp32 chunked scan (VALU), P <= 64, N <= 128, Q <= 256.
 hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                            int64_t Q, const float *x, const float *dt, const float *A,

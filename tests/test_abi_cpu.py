@@ -128,3 +128,38 @@ def test_state_init_validation(lib):
     assert lib.ssd_state_init(ctypes.byref(d), None, None, None) == 1
     assert lib.ssd_state_init(ctypes.byref(d), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 64), None) == 4
     assert lib.ssd_state_init(ctypes.byref(dims(batch=0)), None, None, None) == 0
+
+
+def test_decode_steps_validation(lib):
+    p = ctypes.c_void_p
+    d = dims()
+    # x, dt, A, B, C, D, state, y: 8 GiB apart, well beyond 1000 steps of the 2.7B shape
+    base = [p(FAKE + (k << 33)) for k in range(8)]
+
+    def call(*over, steps=1000, **kw):
+        args = list(base)
+        for i, v in over:
+            args[i] = v
+        return lib.ssd_decode_steps(ctypes.byref(kw.get("d", d)), ctypes.c_int64(steps), *args,
+                                    None)
+
+    assert call((0, None)) == 1
+    assert call((7, None)) == 1
+    assert call(steps=-1) == 2
+    assert call((7, p(FAKE + (6 << 33) + 64))) == 4     # y overlaps the state
+    assert call((6, p(FAKE + 64))) == 4                 # state overlaps x
+    # y [S, B, H, P] bf16 spans S x 40960 bytes at batch 4: 1000 steps of it
+    # (41 MB) reach x placed 16 MiB after it, where one step's slice ends well before
+    assert call((7, p(FAKE + (1 << 32))), (0, p(FAKE + (1 << 32) + (1 << 24)))) == 4
+    assert call((1, p(FAKE + (7 << 33) + 4096))) == 4   # dt inside y
+    assert call(d=dims(dstate=96)) == 3
+    assert call(d=dims(headdim=(1 << 24) + 1)) == 3
+    assert call(d=dims(ngroups=7)) == 2
+    assert call(steps=1 << 31) == 3
+    assert call((6, p(FAKE + (6 << 33) + 4))) == 7      # misaligned state
+    assert call((3, p(FAKE + (3 << 33) + 8))) == 7      # misaligned B
+    assert call((0, p(FAKE + 1))) == 7                  # x not element-aligned
+    assert lib.ssd_decode_steps(ctypes.byref(dims(batch=0)), ctypes.c_int64(5), *([None] * 8),
+                                None) == 0
+    assert lib.ssd_decode_steps(ctypes.byref(d), ctypes.c_int64(0), *([None] * 8), None) == 0
+    assert lib.ssd_decode_steps(None, ctypes.c_int64(1), *([None] * 8), None) == 1
