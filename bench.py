@@ -9,7 +9,9 @@ prefill tokens/s (batch x seqlen per step time).  The decode half of the
 metric (1000 in-place ssd_decode_step calls on a [256, 80, 64, 128] fp32 state,
 fresh tokens each step) is reported under ``decode``; batches 1, 16, 64 are
 reported as effective bandwidth (their state fits in the 256 MB MALL or the
-step is launch-bound).
+step is launch-bound).  ``decode_steps`` runs the same 1000 steps as one
+ssd_decode_steps launch (state held on-chip across the steps), whose bound is
+fp32 VALU arithmetic.
 
 Prints ONE JSON line.  ``roofline`` is the dominant prefill kernel
 (chunk_scan_kernel): algorithmic bytes of the layer per launch / its average
@@ -35,9 +37,11 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s (256 CU x 2.4 GHz x 256 FLOP/clk)
 METRIC = "SSD prefill tokens/s (MFMA %) + decode steps/s (HBM GB/s %) at 2.7B-layer shape"
 KERNEL_SOURCES = ["state_space_model_mamba_amd/csrc/ssd_scan_bf16.hip",
-                  "state_space_model_mamba_amd/csrc/ssd_decode.hip"]
+                  "state_space_model_mamba_amd/csrc/ssd_decode.hip",
+                  "state_space_model_mamba_amd/csrc/ssd_decode_steps.hip"]
 
 
 def prefill_bytes(w) -> int:
@@ -65,6 +69,13 @@ def decode_bytes(b, w) -> int:
     """HBM bytes of one decode step: state read + write, x, y, B, C, dt."""
     state = b * w.nheads * w.headdim * w.dstate * 4
     return 2 * state + 2 * b * w.nheads * w.headdim * 2 + 2 * b * w.ngroups * w.dstate * 2 + b * w.nheads * 4
+
+
+def decode_steps_flops(b, w) -> int:
+    """Arithmetic of one decode step: per state element alpha*H, u*B, their sum,
+    H*C and its accumulation (5 FLOP); per state row dt*x, D*x and its add (3)."""
+    rows = b * w.nheads * w.headdim
+    return rows * (5 * w.dstate + 3)
 
 
 def source_digest() -> str:
@@ -107,7 +118,7 @@ def _counter_means(path, counter):
             copy += v
         short = name.split("(")[0].split("::")[-1]
         for k in ("seg_state_kernel", "chunk_scan_kernel", "decode_rows_kernel",
-                  "decode_kernel", "scan_f32_kernel"):
+                  "decode_steps_kernel", "decode_kernel", "scan_f32_kernel"):
             if k in short or k in name:
                 per.setdefault(k, []).append(v)
                 break
@@ -270,6 +281,23 @@ def bench_decode(args):
         out[b].update({"graph_ms_per_step": gwall * 1e3 / steps, "graph_steps_per_s": steps / gwall,
                        "graph_gbs": nb / (g_ms * 1e-3) / 1e9})
         del graph
+        # the same steps as one ssd_decode_steps launch (state read and written once)
+        ssd.ssd_decode_steps(x, dt, dA, B, C, dD, state, y=y)
+        torch.cuda.synchronize()
+        reps = 3
+        t0 = time.perf_counter()
+        e0.record()
+        for _ in range(reps):
+            ssd.ssd_decode_steps(x, dt, dA, B, C, dD, state, y=y)
+        e1.record()
+        torch.cuda.synchronize()
+        mwall = time.perf_counter() - t0
+        m_ms = e0.elapsed_time(e1) / (reps * steps)
+        fl = decode_steps_flops(b, w)
+        out[b].update({"steps_launch_ms_per_step": mwall * 1e3 / (reps * steps),
+                       "steps_launch_steps_per_s": reps * steps / mwall,
+                       "steps_launch_event_ms_per_step": m_ms,
+                       "steps_launch_tflops": fl / (m_ms * 1e-3) / 1e12})
         del x, dt, B, C, y, state
         torch.cuda.empty_cache()
     return w, out
@@ -414,8 +442,32 @@ def main():
                     "launch-bound: effective bandwidth, not HBM; graph_*: the same steps "
                     "replayed from one captured HIP graph",
         }
+        fl = decode_steps_flops(main_b, wd)
+        m_ms = d["steps_launch_event_ms_per_step"]
+        line["decode_steps"] = {
+            "workload": f"ssd_decode_steps at the 2.7B shape: the same {d['steps']} steps on a "
+                        f"[{main_b},80,64,128] fp32 state as one launch (state read and written "
+                        f"once, held in registers across the steps)",
+            "steps_per_s": d["steps_launch_steps_per_s"],
+            "ms_per_step": d["steps_launch_ms_per_step"],
+            "roofline": {"bound": "alu", "kernel": "decode_steps_kernel",
+                         "achieved": fl / (m_ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                         "unit": "TFLOP/s",
+                         "frac": fl / (m_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                         "traffic": committed_traffic("decode_steps_kernel"),
+                         "flops_per_step": fl, "avg_launch_ms": m_ms * d["steps"]},
+            "batches": {str(b): {"steps_per_s": r["steps_launch_steps_per_s"],
+                                 "ms_per_step": r["steps_launch_ms_per_step"],
+                                 "event_ms_per_step": r["steps_launch_event_ms_per_step"],
+                                 "tflops": r["steps_launch_tflops"]}
+                        for b, r in sorted(dec.items())},
+        }
         if not args.no_cpu_baseline:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(wd)
+            line["decode_steps"]["cpu_baseline"] = dict(
+                line["decode"]["cpu_baseline"],
+                sample=line["decode"]["cpu_baseline"]["sample"] + " (the oracle has one decode "
+                       "form: the same run serves both)")
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(w)
     print(json.dumps(line), flush=True)

@@ -14,17 +14,22 @@
 // and stores them once.  Per step only that step's x, dt, B, C come in and y
 // goes out, so the work is fp32 VALU arithmetic on registers.
 //
-// Layout of a wave: a state row (N floats) is spread over LPR = min(N, 64)
-// lanes with CPL = N / LPR consecutive columns each; a wave holds RPW = 64 /
-// LPR row groups of R rows, so every lane owns R x CPL state elements.  The
-// reduction of y over n is done per lane over its CPL columns, then across the
-// LPR lanes of a row group without going through LDS: first log2(R) halving
-// exchanges (permlane32 / permlane16 swaps, then DPP mirrors and quad
-// permutations), each of which leaves a lane with half as many rows summed
-// over twice as many lanes, then plain DPP sums over the remaining lane bits.
-// Afterwards the lanes of row group `grp` with lane-in-row index lr hold the
-// full sum for row slot lr >> SHIFT.
+// Layout of a wave: a state row (N floats) is spread over LPR lanes with
+// CPL = N / LPR consecutive columns each: LPR = 16 (one DPP row) for
+// N <= 128, LPR = 64 for N = 256.  A wave holds RPW = 64 / LPR row groups of
+// R rows, so every lane owns R x CPL state elements.  The reduction of y over
+// n is done per lane over its CPL columns, then across the LPR lanes of a row
+// group without going through LDS: first log2(R) halving exchanges
+// (permlane32 / permlane16 swaps, then DPP mirrors and quad permutations),
+// each of which leaves a lane with half as many rows summed over twice as
+// many lanes, then plain DPP sums over the remaining lane bits.  Afterwards
+// the lanes of row group `grp` with lane-in-row index lr hold the full sum
+// for row slot lr >> SHIFT.  Fewer lanes per row make that reduction short
+// (4 exchanges for 4 rows over 16 lanes, against 35 instructions for 16 rows
+// over 64 lanes) at the price of unpacking more B and C values per lane.
 #include <hip/hip_runtime.h>
+
+#include <type_traits>
 
 #include "ssd_kernels.h"
 
@@ -34,15 +39,15 @@ namespace {
 constexpr int kStepsThreads = 256;   // four independent waves per work-group
 constexpr int kStepsAhead = 4;       // decode steps whose inputs are in flight
 
-template <int N, int R>
+template <int N, int CPL, int R>
 struct StepsGeom {
-    static constexpr int LPR = N < 64 ? N : 64;    // lanes per state row
-    static constexpr int CPL = N / LPR;            // consecutive columns per lane
+    static constexpr int LPR = N / CPL;            // lanes per state row
     static constexpr int RPW = 64 / LPR;           // row groups per wave
     static constexpr int LOG_LPR = __builtin_ctz(LPR);
     static constexpr int HALVE = __builtin_ctz(R); // halving exchanges of the y reduction
     static constexpr int SHIFT = LOG_LPR - HALVE;  // a row's sum ends on 1 << SHIFT lanes
     static constexpr int ROWS = R * RPW;           // state rows per wave
+    static_assert(LPR == 16 || LPR == 64, "a row spans one DPP row or the whole wave");
     static_assert((R & (R - 1)) == 0 && R >= 1 && R <= LPR, "R: power of two <= LPR");
 };
 
@@ -58,12 +63,15 @@ __device__ __forceinline__ rsrc_t buf(const void *base, int bytes)
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, bytes, 0x00020000);
 }
 
-// kBytes (2, 4, 8 or 16) bytes at byte offset off, as raw 32-bit words.
+// kBytes (2, 4, 8, 16 or 32) bytes at byte offset off, as raw 32-bit words.
 template <int kBytes>
 struct Raw {
     static constexpr int W = kBytes < 4 ? 1 : kBytes / 4;
     unsigned w[W];
 };
+
+template <int kBytes>
+__device__ __forceinline__ Raw<kBytes> load_raw(rsrc_t r, unsigned off);
 
 template <int kBytes>
 __device__ __forceinline__ Raw<kBytes> load_raw(rsrc_t r, unsigned off)
@@ -77,12 +85,20 @@ __device__ __forceinline__ Raw<kBytes> load_raw(rsrc_t r, unsigned off)
         const u32x2 t = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
         v.w[0] = t[0];
         v.w[1] = t[1];
-    } else {
-        static_assert(kBytes == 16, "2, 4, 8 or 16 bytes");
+    } else if constexpr (kBytes == 16) {
         const u32x4 t = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
             v.w[i] = t[i];
+    } else {
+        static_assert(kBytes == 32, "2, 4, 8, 16 or 32 bytes");
+        const u32x4 t0 = __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        const u32x4 t1 = __builtin_amdgcn_raw_buffer_load_b128(r, off + 16, 0, 0);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v.w[i] = t0[i];
+            v.w[4 + i] = t1[i];
+        }
     }
     return v;
 }
@@ -114,6 +130,13 @@ __device__ __forceinline__ float dpp(float v)
 {
     return __builtin_bit_cast(
         float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl, 0xf, 0xf, true));
+}
+
+// Lane kLane of each 16-lane row, broadcast to the row (gfx90a+ DPP row_newbcast).
+template <int kLane>
+__device__ __forceinline__ float row_bcast(float v)
+{
+    return dpp<0x150 + kLane>(v);
 }
 
 // DPP control of the exchange partner for lane bits 0..3: quad permutations
@@ -205,6 +228,20 @@ __device__ __forceinline__ float reduce_rows(float (&v)[R], int lane)
     return pair_sums<0, Gm::SHIFT>(v[0]);
 }
 
+// u[s] = v of lane s << SHIFT of the lane's row group, s < R.
+template <class Gm, int kS, int R>
+__device__ __forceinline__ void bcast_rows(float (&u)[R], float v)
+{
+    if constexpr (kS < R) {
+        if constexpr (Gm::LPR == 64)
+            u[kS] = __builtin_bit_cast(
+                float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kS << Gm::SHIFT));
+        else
+            u[kS] = row_bcast<(kS << Gm::SHIFT)>(v);
+        bcast_rows<Gm, kS + 1>(u, v);
+    }
+}
+
 // The inputs of one decode step as this lane needs them.
 template <typename T, int CPL>
 struct StepIn {
@@ -215,15 +252,21 @@ struct StepIn {
 
 // One work-group = four waves, each an independent block of ROWS state rows of
 // one (batch row, head); `wpb` waves cover the P rows of a pair.
-template <typename T, int N, int R>
-__global__ __launch_bounds__(kStepsThreads) void decode_steps_kernel(
+// Waves per SIMD the compiler must leave room for: the bf16 kernels are held
+// to three (168 registers) so that the large row blocking still overlaps three
+// waves on a SIMD; the fp32 ones keep their larger prefetch ring in registers.
+template <typename T>
+constexpr int kStepsMinWaves = sizeof(T) == 2 ? 3 : 1;
+
+template <typename T, int N, int CPL, int R>
+__global__ __attribute__((amdgpu_flat_work_group_size(1, kStepsThreads),
+                          amdgpu_waves_per_eu(kStepsMinWaves<T>))) void decode_steps_kernel(
     int S, int Bn, int H, int P, int G, int wpb, const T *__restrict__ x,
     const float *__restrict__ dt, const float *__restrict__ A, const T *__restrict__ Bm,
     const T *__restrict__ Cm, const float *__restrict__ D, float *__restrict__ state,
     T *__restrict__ y)
 {
-    using Gm = StepsGeom<N, R>;
-    constexpr int CPL = Gm::CPL;
+    using Gm = StepsGeom<N, CPL, R>;
     constexpr int esz = (int)sizeof(T);
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / 64);
     const int lane = (int)threadIdx.x % 64;
@@ -266,67 +309,111 @@ __global__ __launch_bounds__(kStepsThreads) void decode_steps_kernel(
     const bool writer = (lr & ((1 << Gm::SHIFT) - 1)) == 0;
     const unsigned yoff = writer ? xoff : 0x7fffffffu;
 
-    // running pointers at the next step to issue; they stop at the last step,
-    // and a step past it gets empty resources (its loads read zeros)
+    // Running pointers at the next step to issue.  A checked issue may be past
+    // the last step: its pointers stay at the last step and its resources are
+    // empty (its loads read zeros); an unchecked one is known to be in range.
     const T *xi = xb, *bi = bb, *ci = cb;
     const float *di = db;
     int ti = 0;
-    auto issue = [&](StepIn<T, CPL> &in) {
-        const bool ok = ti < S;
+    auto issue = [&](StepIn<T, CPL> &in, auto checked) {
+        bool ok = true, more = true;
+        if constexpr (decltype(checked)::value) {
+            ok = ti < S;
+            more = ti + 1 < S;
+        }
         in.x = load_raw<esz>(buf(xi, ok ? P * esz : 0), xoff);
         in.dt = load_raw<4>(buf(di, ok ? 4 : 0), 0);
         in.B = load_raw<CPL * esz>(buf(bi, ok ? N * esz : 0), boff);
         in.C = load_raw<CPL * esz>(buf(ci, ok ? N * esz : 0), boff);
-        const bool more = ti + 1 < S;
         xi = more ? xi + xstep : xi;
         di = more ? di + dstep : di;
         bi = more ? bi + bstep : bi;
         ci = more ? ci + bstep : ci;
         ++ti;
     };
+    using checked_t = std::integral_constant<bool, true>;
+    using unchecked_t = std::integral_constant<bool, false>;
 
+    // With the large row blocking (throughput-bound; 16 or more state elements
+    // per lane) the lanes keep H / sc, sc
+    // being the product of the decays since the last renormalisation (the
+    // same on every lane of the wave), so that a step is one fused
+    // multiply-add per element: H/sc' += (dt x / sc') B with sc' = sc alpha,
+    // and y = sc' (H/sc' . C) + D x.  A step that would take sc outside
+    // [2^-64, 2^64] (alpha = 0 included) instead multiplies the state by sc
+    // and alpha and restarts sc at 1.  1 / sc' is the hardware reciprocal
+    // (within 1 ulp).  The small blocking runs one wave per SIMD and is bound
+    // by the latency of a step, so it applies alpha directly (two operations
+    // per element, none of the bookkeeping).
+    constexpr bool kLazy = R * CPL >= 16;
+    float sc = 1.f;
     T *yp = yb;   // y of the step being computed
     auto step = [&](const StepIn<T, CPL> &in) {
         const float xv = elem<T, 1>(in.x, 0);
         const float d = elem<float, 1>(in.dt, 0);
         const float alpha = __expf(d * Ah);
-        const float ux = d * xv;
+        float ux = d * xv, scn = 1.f;
+        if constexpr (kLazy) {
+            scn = sc * alpha;
+            if (__builtin_amdgcn_readfirstlane(!(scn >= 0x1p-64f && scn <= 0x1p64f))) {
+#pragma unroll
+                for (int s = 0; s < R; ++s)
+#pragma unroll
+                    for (int k = 0; k < CPL; ++k)
+                        st[s][k] = st[s][k] * sc * alpha;
+                scn = 1.f;
+            }
+            sc = scn;
+            ux *= __builtin_amdgcn_rcpf(scn);
+        }
+        // dt x (/ sc) of row slot s of this lane's group, held by the group's
+        // lane s << SHIFT: a readlane when a row spans the wave, a DPP row
+        // broadcast when it spans a 16-lane row
+        float u[R];
+        bcast_rows<Gm, 0>(u, ux);
         float part[R];
 #pragma unroll
         for (int s = 0; s < R; ++s) {
-            // dt * x of row slot s of this lane's group (held by lane s << SHIFT)
-            float u;
-            if constexpr (Gm::RPW == 1)
-                u = __builtin_bit_cast(
-                    float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, ux), s << Gm::SHIFT));
-            else
-                u = __shfl(ux, grp * Gm::LPR + (s << Gm::SHIFT), 64);
             float acc = 0.f;
 #pragma unroll
             for (int k = 0; k < CPL; ++k) {
-                const float o = alpha * st[s][k] + u * elem<T, CPL>(in.B, k);
+                const float o = kLazy ? __builtin_fmaf(u[s], elem<T, CPL>(in.B, k), st[s][k])
+                                      : alpha * st[s][k] + u[s] * elem<T, CPL>(in.B, k);
                 st[s][k] = o;
                 acc = k == 0 ? o * elem<T, CPL>(in.C, k) : acc + o * elem<T, CPL>(in.C, k);
             }
             part[s] = acc;
         }
-        const float yv = reduce_rows<Gm>(part, lane) + Dh * xv;
+        const float sum = reduce_rows<Gm>(part, lane);
+        const float yv = (kLazy ? sum * scn : sum) + Dh * xv;
         store_y<T>(buf(yp, P * esz), yoff, yv);
         yp += xstep;
     };
 
+    // Inputs are issued kStepsAhead steps ahead of the one computed: a ring of
+    // loads in flight.  Groups of steps whose issues all stay in range run
+    // unchecked.
     StepIn<T, CPL> ring[kStepsAhead];
 #pragma unroll
     for (int k = 0; k < kStepsAhead; ++k)
-        issue(ring[k]);
+        issue(ring[k], checked_t{});
     int t0 = 0;
-    for (; t0 + kStepsAhead <= S; t0 += kStepsAhead) {
+    // a slot is refilled right after the step that consumed it, so the loads
+    // land in the registers it frees (no copies around the loop)
+    for (; t0 + 2 * kStepsAhead <= S; t0 += kStepsAhead) {
 #pragma unroll
         for (int k = 0; k < kStepsAhead; ++k) {
-            const StepIn<T, CPL> cur = ring[k];
-            issue(ring[k]);
-            step(cur);
+            step(ring[k]);
+            issue(ring[k], unchecked_t{});
         }
+    }
+    if (t0 + kStepsAhead <= S) {
+#pragma unroll
+        for (int k = 0; k < kStepsAhead; ++k) {
+            step(ring[k]);
+            issue(ring[k], checked_t{});
+        }
+        t0 += kStepsAhead;
     }
 #pragma unroll
     for (int k = 0; k < kStepsAhead - 1; ++k)
@@ -339,43 +426,46 @@ __global__ __launch_bounds__(kStepsThreads) void decode_steps_kernel(
         if (row < P) {
 #pragma unroll
             for (int k = 0; k < CPL; ++k)
-                sp[(int64_t)row * N + k] = st[s][k];
+                sp[(int64_t)row * N + k] = st[s][k] * sc;
         }
     }
 }
 
-// Rows per lane: the larger choice keeps 16 rows (32 state elements at
-// N = 128); the smaller one, a quarter of it, spreads a small batch over four
-// times as many waves, and is used while the larger would leave the chip with
-// fewer than two waves per SIMD.
+// Layouts: a state row spans one 16-lane DPP row (CPL = N / 16 columns per
+// lane) for N <= 128, the whole wave for N = 256.  Rows per lane: the larger
+// choice keeps 32 state elements per lane (16 for N = 16); the smaller one, a
+// quarter of it, spreads a small batch over four times as many waves, and is
+// used while the larger would leave the chip with fewer than two waves per
+// SIMD.
 constexpr int kSmallBatchWaves = 2048;
 
-template <typename T, int N, int R>
+template <typename T, int N, int CPL, int R>
 hipError_t launch_steps(int64_t S, int64_t B, int64_t H, int64_t P, int64_t G, const void *x,
                         const float *dt, const float *A, const void *Bm, const void *Cm,
                         const float *D, float *state, void *y, hipStream_t s)
 {
-    const int64_t wpb = (P + StepsGeom<N, R>::ROWS - 1) / StepsGeom<N, R>::ROWS;
+    using Gm = StepsGeom<N, CPL, R>;
+    const int64_t wpb = (P + Gm::ROWS - 1) / Gm::ROWS;
     const int64_t waves = B * H * wpb;
     if (waves > INT32_MAX - 4)
         return hipErrorInvalidValue;
     const int64_t blocks = (waves + kStepsThreads / 64 - 1) / (kStepsThreads / 64);
-    decode_steps_kernel<T, N, R><<<(unsigned)blocks, kStepsThreads, 0, s>>>(
+    decode_steps_kernel<T, N, CPL, R><<<(unsigned)blocks, kStepsThreads, 0, s>>>(
         (int)S, (int)B, (int)H, (int)P, (int)G, (int)wpb, static_cast<const T *>(x), dt, A,
         static_cast<const T *>(Bm), static_cast<const T *>(Cm), D, state, static_cast<T *>(y));
     return hipGetLastError();
 }
 
-template <typename T, int N, int RBig>
+template <typename T, int N, int CPL, int RBig>
 hipError_t steps_select(int64_t S, int64_t B, int64_t H, int64_t P, int64_t G, const void *x,
                         const float *dt, const float *A, const void *Bm, const void *Cm,
                         const float *D, float *state, void *y, hipStream_t s)
 {
     constexpr int RSmall = RBig / 4;
-    const int64_t rows = StepsGeom<N, RBig>::ROWS;
+    const int64_t rows = StepsGeom<N, CPL, RBig>::ROWS;
     if (B * H * ((P + rows - 1) / rows) < kSmallBatchWaves)
-        return launch_steps<T, N, RSmall>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    return launch_steps<T, N, RBig>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+        return launch_steps<T, N, CPL, RSmall>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+    return launch_steps<T, N, CPL, RBig>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
 }
 
 template <typename T>
@@ -384,11 +474,11 @@ hipError_t steps_dispatch(int64_t S, int64_t B, int64_t H, int64_t P, int64_t N,
                           const void *Cm, const float *D, float *state, void *y, hipStream_t s)
 {
     switch (N) {
-    case 16: return steps_select<T, 16, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 32: return steps_select<T, 32, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 64: return steps_select<T, 64, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 128: return steps_select<T, 128, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 256: return steps_select<T, 256, 8>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+    case 16: return steps_select<T, 16, 1, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+    case 32: return steps_select<T, 32, 2, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+    case 64: return steps_select<T, 64, 4, 8>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+    case 128: return steps_select<T, 128, 8, 4>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+    case 256: return steps_select<T, 256, 4, 8>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
     default: return hipErrorInvalidValue;
     }
 }

@@ -132,3 +132,44 @@ def test_decode_steps_graph_replay():
         torch.cuda.synchronize()
         assert np.array_equal(host(ys), y_ref), f"replay {rep}: y"
         assert np.array_equal(host(state), s_ref), f"replay {rep}: state"
+
+
+def _steps_with_heads(A, dt_scale, seed, steps, io="bf16", batch=3):
+    """decode_steps with chosen per-head A and dt scaled by dt_scale, against the
+    oracle on the same values (all sequences)."""
+    H = len(A)
+    w = si.small_workload(batch=batch, seqlen=0, nheads=H, io=io, seed=seed)
+    tok = si.decode_tokens(w, batch, 0, steps)
+    tok["dt"] = (tok["dt"] * np.float32(dt_scale)).astype(np.float32)
+    A = np.asarray(A, dtype=np.float32)
+    _, D = si.head_params(w)
+    state0 = si.random_state(w, batch)
+    x, dt, B, C = dev(tok["x"], io), dev(tok["dt"]), dev(tok["B"], io), dev(tok["C"], io)
+    state = dev(state0.copy())
+    ys = ssd.ssd_decode_steps(x, dt, dev(A), B, C, dev(D), state)
+    torch.cuda.synchronize()
+    yref, sref = oracle_decode(w, tok, A.astype(np.float64), D, state0, list(range(batch)))
+    y, s = host(ys), host(state)
+    assert np.isfinite(y).all() and np.isfinite(s).all()
+    check_y(y.transpose(1, 0, 2, 3), yref, TOL[io], "decay y")
+    check_state(s, sref, TOL[io], "decay state")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_steps_extreme_decay(io):
+    """A = -1e6: alpha underflows to 0 on every step, so every step folds the
+    scale back and the state is memoryless: H_t = dt_t x_t (outer) B_t."""
+    _steps_with_heads([-1e6, -1e6, -5e5, -1e6], 1.0, seed=41, steps=11, io=io)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_steps_no_decay(io):
+    """A = 0: alpha = 1, the scale never moves and the state is a running sum."""
+    _steps_with_heads([0.0, 0.0, 0.0], 1.0, seed=42, steps=300, io=io)
+
+
+def test_decode_steps_decay_mix():
+    """Heads from no decay to strong decay over many steps, so that the state
+    scale is renormalised every few steps, rarely, or never, head by head."""
+    _steps_with_heads([0.0, -0.05, -1.0, -16.0, -100.0, -3.0, -0.5, -40.0], 1.0, seed=43, steps=400)
+    _steps_with_heads([-16.0, -8.0, -4.0, -1.0], 10.0, seed=44, steps=90)
