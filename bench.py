@@ -199,6 +199,20 @@ def bench_prefill(args):
         for name, t in times:
             per.setdefault(name, []).append(t)
     kern = {k: float(np.mean(v)) for k, v in per.items()}
+    # the same step with the fused step-size prep (dt read as u, softplus(u + bias)
+    # formed in the kernels); u and the bias are arbitrary here, only time matters
+    bias = torch.zeros(w.nheads, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
+                           dt_softplus=True, dt_bias=bias)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(args.steps):
+        ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
+                           dt_softplus=True, dt_bias=bias)
+    e1.record()
+    torch.cuda.synchronize()
+    sp_ms = e0.elapsed_time(e1) / args.steps
     nbytes = prefill_bytes(w)
     flops = prefill_useful_flops(w)
     k3 = kern["chunk_scan_kernel"]
@@ -221,6 +235,7 @@ def bench_prefill(args):
                     "rocprof MFMA busy counters are in profiles/",
         },
         "path_gbs": nbytes / (ms * 1e-3) / 1e9,
+        "dt_softplus_event_ms_per_step": sp_ms,
     }
     return res
 
@@ -423,6 +438,10 @@ def main():
         "path_gbs": pre["path_gbs"],
         "roofline": pre["roofline"],
         "mfma": pre["mfma"],
+        "prefill_fused_dt_softplus": {
+            "event_ms_per_step": pre["dt_softplus_event_ms_per_step"],
+            "note": "the same prefill with dt passed as u and softplus(u + dt_bias) formed "
+                    "inside the scan kernels (ssd_dims.flags = SSD_DT_SOFTPLUS)"},
     }
     if not args.no_decode:
         wd, dec = bench_decode(args)

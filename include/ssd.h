@@ -67,8 +67,16 @@ typedef enum ssd_dtype {
     SSD_BF16 = 1             /* x, B, C, y in bfloat16                            */
 } ssd_dtype;
 
-/* Problem sizes.  seqlen and chunk are ignored by ssd_decode_step and
- * ssd_state_init.  reserved must be 0. */
+/* flags of ssd_dims: fused step-size prep.  With SSD_DT_SOFTPLUS the dt
+ * argument of every call holds u instead of the step size, and the step size
+ * of head h is softplus(u + dt_bias[h]) = log(1 + exp(u + dt_bias[h])),
+ * evaluated in fp32 inside the kernels (the workloads draw dt through a
+ * softplus; fusing it saves a pass over dt).  Positions past the end of a
+ * sequence still contribute nothing. */
+#define SSD_DT_SOFTPLUS 1
+
+/* Problem sizes.  seqlen and chunk are ignored by ssd_decode_step(s) and
+ * ssd_state_init. */
 typedef struct ssd_dims {
     int64_t batch;     /* B >= 0                                              */
     int64_t seqlen;    /* L >= 0 tokens per sequence                          */
@@ -78,7 +86,10 @@ typedef struct ssd_dims {
     int64_t ngroups;   /* G >= 1, H % G == 0; head h reads B/C group h/(H/G)  */
     int64_t chunk;     /* Q >= 1, chunk length of the chunked scan            */
     int32_t io_dtype;  /* ssd_dtype of x, B, C, y                             */
-    int32_t reserved;  /* must be 0                                           */
+    int32_t flags;     /* 0 or SSD_DT_SOFTPLUS; other bits: SSD_ERR_SHAPE     */
+    const float *dt_bias; /* [H] fp32 device pointer or NULL (bias 0); read
+                             only with SSD_DT_SOFTPLUS; 4-byte aligned, must
+                             not overlap an output                          */
 } ssd_dims;
 
 /* Human-readable name of a status code (static storage; never NULL). */

@@ -92,6 +92,21 @@ def ssd_scan(x, dt, A, B, C, D, h0=None, nthreads: int = 1, lib=None):
     return y, hL
 
 
+def dt_softplus(u, bias=None):
+    """Step size of the fused input prep: softplus(u + bias) = log(1 + exp(u + bias))
+    in fp64, with bias per head (the last axis of u) or None.
+
+    The workloads draw the step size through a softplus of a uniform u; the
+    library can take u and a per-head bias instead of the step size and form
+    it in its kernels.  Written as the plain definition with numpy's
+    log(exp(0) + exp(v)), which is evaluated without overflow.
+    """
+    v = np.asarray(u, dtype=np.float64)
+    if bias is not None:
+        v = v + np.asarray(bias, dtype=np.float64)
+    return np.logaddexp(0.0, v)
+
+
 def ssd_decode_step(state, x, dt, A, B, C, D, nthreads: int = 1, lib=None):
     """One more iteration of the recurrence on a cached state.
 

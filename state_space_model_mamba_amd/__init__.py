@@ -6,7 +6,8 @@ kernels of ``libssd.so`` (C ABI in ``include/ssd.h``).  PyTorch provides device
 memory and the stream.  There is no fallback: if the library is missing, or a
 call fails, an exception is raised.
 
-Functions keep the C names:
+Functions keep the C names (each call also takes dt_softplus=True, dt_bias=[H]
+to pass u instead of dt; the step size is then softplus(u + dt_bias) in the kernels):
     ssd_state_init(state, src=None)
     ssd_chunk_scan_workspace_size(...)
     ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, ...) -> (y, final_state)
@@ -23,6 +24,7 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG, "libssd.so")
 
 SSD_F32, SSD_BF16 = 0, 1
+SSD_DT_SOFTPLUS = 1            # ssd_dims.flags: dt holds u, the step size is softplus(u + dt_bias)
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_ALIAS", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_DEVICE", 7: "SSD_ERR_ALIGNMENT"}
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_state_init", "ssd_chunk_scan_workspace_size",
@@ -40,7 +42,7 @@ class SsdDims(ctypes.Structure):
                 ("nheads", ctypes.c_int64), ("headdim", ctypes.c_int64),
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("flags", ctypes.c_int32), ("dt_bias", ctypes.c_void_p)]
 
 
 _lib = None
@@ -107,8 +109,13 @@ def _io_dtype(t):
     raise TypeError(f"x/B/C must be bfloat16 or float32, got {t.dtype}")
 
 
-def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype) -> SsdDims:
-    return SsdDims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype, 0)
+def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype,
+              dt_softplus=False, dt_bias=None) -> SsdDims:
+    """ssd_dims; with dt_softplus the dt arguments hold u and the step size is
+    softplus(u + dt_bias[h]) (dt_bias: a [H] fp32 device tensor or None)."""
+    flags = SSD_DT_SOFTPLUS if dt_softplus else 0
+    bias = dt_bias.data_ptr() if (dt_softplus and dt_bias is not None) else None
+    return SsdDims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype, flags, bias)
 
 
 def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups, chunk,
@@ -129,12 +136,13 @@ def ssd_state_init(state, src=None, stream=None):
     return state
 
 
-def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace):
+def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
+               dt_softplus=False, dt_bias=None):
     import torch
     bsz, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     io = _io_dtype(x)
-    d = make_dims(bsz, L, H, P, N, G, chunk, io)
+    d = make_dims(bsz, L, H, P, N, G, chunk, io, dt_softplus, dt_bias)
     if y is None:
         y = torch.empty_like(x)
     if final_state is None:
@@ -149,17 +157,19 @@ def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspac
 
 
 def ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_state=None,
-                   workspace=None, stream=None):
+                   workspace=None, stream=None, dt_softplus=False, dt_bias=None):
     """Prefill over x[B, L, H, P]; returns (y, final_state)."""
-    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace)
+    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
+                             dt_softplus, dt_bias)
     _check("ssd_chunk_scan", load().ssd_chunk_scan(*args, _stream(stream)))
     return y, fs
 
 
 def ssd_chunk_scan_timed(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_state=None,
-                         workspace=None, stream=None):
+                         workspace=None, stream=None, dt_softplus=False, dt_bias=None):
     """As ssd_chunk_scan, synchronously, also returning [(kernel name, ms), ...]."""
-    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace)
+    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
+                             dt_softplus, dt_bias)
     cap = 8
     ms = (ctypes.c_float * cap)()
     names = (ctypes.c_char_p * cap)()
@@ -169,12 +179,13 @@ def ssd_chunk_scan_timed(x, dt, A, B, C, D, chunk, initial_state=None, y=None, f
     return y, fs, [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 
-def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
+def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=False,
+                    dt_bias=None):
     """One decode step: x[B, H, P], B/C[B, G, N], state[B, H, P, N] updated in place; returns y."""
     import torch
     bsz, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
-    d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x))
+    d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x), dt_softplus, dt_bias)
     if y is None:
         y = torch.empty_like(x)
     _check("ssd_decode_step", load().ssd_decode_step(
@@ -183,13 +194,14 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None):
     return y
 
 
-def ssd_decode_steps(x, dt, A, B, C, D, state, y=None, stream=None):
+def ssd_decode_steps(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=False,
+                     dt_bias=None):
     """S decode steps in one launch: x[S, B, H, P], dt[S, B, H], B/C[S, B, G, N];
     state[B, H, P, N] updated in place (read and written once); returns y[S, B, H, P]."""
     import torch
     nsteps, bsz, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
-    d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x))
+    d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x), dt_softplus, dt_bias)
     if y is None:
         y = torch.empty_like(x)
     _check("ssd_decode_steps", load().ssd_decode_steps(

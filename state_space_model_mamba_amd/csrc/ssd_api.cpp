@@ -46,7 +46,7 @@ ssd_status check_dims(const ssd_dims *d, bool uses_chunk)
 {
     if (!d)
         return SSD_ERR_NULL;
-    if (d->reserved != 0)
+    if ((d->flags & ~SSD_DT_SOFTPLUS) != 0)
         return SSD_ERR_SHAPE;
     if (d->batch < 0 || d->nheads < 1 || d->headdim < 1 || d->dstate < 1 || d->ngroups < 1)
         return SSD_ERR_SHAPE;
@@ -89,6 +89,28 @@ bool overlap(Span a, Span b)
 bool aligned(const void *p, uintptr_t n)
 {
     return reinterpret_cast<uintptr_t>(p) % n == 0;
+}
+
+ssd::DtPrep dt_prep(const ssd_dims *d)
+{
+    const bool sp = (d->flags & SSD_DT_SOFTPLUS) != 0;
+    return ssd::DtPrep{sp ? d->dt_bias : nullptr, sp ? 1 : 0};
+}
+
+// The bias of the fused step-size prep: 4-byte aligned and outside every
+// output span.
+ssd_status check_dt_bias(const ssd_dims *d, const Span *outs, int nouts)
+{
+    const ssd::DtPrep pr = dt_prep(d);
+    if (!pr.bias)
+        return SSD_OK;
+    if (!aligned(pr.bias, 4))
+        return SSD_ERR_ALIGNMENT;
+    const Span sb = span(pr.bias, d->nheads * 4);
+    for (int i = 0; i < nouts; ++i)
+        if (overlap(sb, outs[i]))
+            return SSD_ERR_ALIAS;
+    return SSD_OK;
 }
 
 ssd_status device_status(hipError_t e)
@@ -167,17 +189,20 @@ ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const flo
             return SSD_ERR_ALIAS;
     if (overlap(sws, sfin) || overlap(sws, sinit))
         return SSD_ERR_ALIAS;
+    const Span outs[] = {sy, sfin, sws};
+    if ((st = check_dt_bias(d, outs, 3)) != SSD_OK)
+        return st;
 
     hipError_t e;
     if (d->io_dtype == SSD_BF16) {
         const ssd::Bf16Plan plan = ssd::plan_scan_bf16(Bn, L, H, G, d->chunk);
         e = ssd::launch_scan_bf16(plan, Bn, L, H, G, d->chunk, x, dt, A, B, C, D, init, y, fin,
-                                  ws, s, log);
+                                  ws, dt_prep(d), s, log);
     } else {
         e = ssd::launch_scan_f32(Bn, L, H, P, N, G, d->chunk, static_cast<const float *>(x), dt,
                                  A, static_cast<const float *>(B),
                                  static_cast<const float *>(C), D, init,
-                                 static_cast<float *>(y), fin, s, log);
+                                 static_cast<float *>(y), fin, dt_prep(d), s, log);
     }
     return device_status(e);
 }
@@ -201,7 +226,7 @@ SSD_EXPORT const char *ssd_status_string(ssd_status status)
 
 SSD_EXPORT int ssd_version(void)
 {
-    return 10000;
+    return 10100;
 }
 
 SSD_EXPORT ssd_status ssd_state_init(const ssd_dims *dims, float *state, const float *src,
@@ -320,8 +345,12 @@ SSD_EXPORT ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const
             return SSD_ERR_ALIAS;
     if (overlap(sy, ss))
         return SSD_ERR_ALIAS;
+    const Span outs[] = {sy, ss};
+    if ((st = check_dt_bias(dims, outs, 2)) != SSD_OK)
+        return st;
     return device_status(ssd::launch_decode(dims->io_dtype == SSD_BF16, Bn, H, P, N, G, x, dt, A,
-                                            B, C, D, state, y, static_cast<hipStream_t>(stream)));
+                                            B, C, D, state, y, dt_prep(dims),
+                                            static_cast<hipStream_t>(stream)));
 }
 
 SSD_EXPORT ssd_status ssd_decode_steps(const ssd_dims *dims, int64_t nsteps, const void *x,
@@ -362,7 +391,10 @@ SSD_EXPORT ssd_status ssd_decode_steps(const ssd_dims *dims, int64_t nsteps, con
             return SSD_ERR_ALIAS;
     if (overlap(sy, ss))
         return SSD_ERR_ALIAS;
+    const Span outs[] = {sy, ss};
+    if ((st = check_dt_bias(dims, outs, 2)) != SSD_OK)
+        return st;
     return device_status(ssd::launch_decode_steps(dims->io_dtype == SSD_BF16, nsteps, Bn, H, P,
                                                   N, G, x, dt, A, B, C, D, state, y,
-                                                  static_cast<hipStream_t>(stream)));
+                                                  dt_prep(dims), static_cast<hipStream_t>(stream)));
 }

@@ -81,7 +81,7 @@ template <typename T, int N, bool kNT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
     int64_t H, int64_t P, int64_t G, const T *__restrict__ x, const float *__restrict__ dt,
     const float *__restrict__ A, const T *__restrict__ Bm, const T *__restrict__ Cm,
-    const float *__restrict__ D, float *__restrict__ state, T *__restrict__ y)
+    const float *__restrict__ D, float *__restrict__ state, T *__restrict__ y, DtPrep prep)
 {
     constexpr int LPR = N / 4;                 // lanes per state row
     constexpr int RPP = kDecodeThreads / LPR;  // rows per pass
@@ -92,7 +92,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_kernel(
 
     const float4 Bv = load4<T>(Bm + (b * G + g) * N + n0);
     const float4 Cv = load4<T>(Cm + (b * G + g) * N + n0);
-    const float d = dt[bh];
+    float d = dt[bh];
+    if (prep.softplus)
+        d = softplus_dt(d, prep.bias ? prep.bias[h] : 0.f);
     const float alpha = __expf(d * A[h]);
     const float Dh = D[h];
     float *S = state + bh * P * N;
@@ -152,7 +154,7 @@ template <typename T, int N, bool kNT>
 __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(
     int H, int P, int G, const T *__restrict__ x, const float *__restrict__ dt,
     const float *__restrict__ A, const T *__restrict__ Bm, const T *__restrict__ Cm,
-    const float *__restrict__ D, float *__restrict__ state, T *__restrict__ y)
+    const float *__restrict__ D, float *__restrict__ state, T *__restrict__ y, DtPrep prep)
 {
     constexpr int LPR = N / 16;                // lanes per state row
     constexpr int RPP = kDecodeThreads / LPR;  // rows per pass
@@ -167,7 +169,9 @@ __global__ __launch_bounds__(kDecodeThreads) void decode_rows_kernel(
         Bv[k] = load4<T>(Bm + (int64_t)(b * G + g) * N + 4 * lr + 4 * LPR * k);
         Cv[k] = load4<T>(Cm + (int64_t)(b * G + g) * N + 4 * lr + 4 * LPR * k);
     }
-    const float d = dt[bh];
+    float d = dt[bh];
+    if (prep.softplus)
+        d = softplus_dt(d, prep.bias ? prep.bias[h] : 0.f);
     const float alpha = __expf(d * A[h]);
     const float Dh = D[h];
     float *S = state + (int64_t)bh * P * N + 4 * lr;
@@ -234,7 +238,7 @@ __global__ void fill4_kernel(float4 *__restrict__ dst, const float4 *__restrict_
 template <typename T, bool kNT>
 hipError_t decode_dispatch(int64_t B, int64_t H, int64_t P, int64_t N, int64_t G, const void *x,
                            const float *dt, const float *A, const void *Bm, const void *Cm,
-                           const float *D, float *state, void *y, hipStream_t s)
+                           const float *D, float *state, void *y, DtPrep prep, hipStream_t s)
 {
     const dim3 grid((unsigned)(B * H)), block(kDecodeThreads);
     const T *xx = static_cast<const T *>(x);
@@ -244,19 +248,19 @@ hipError_t decode_dispatch(int64_t B, int64_t H, int64_t P, int64_t N, int64_t G
     const int h = (int)H, p = (int)P, g = (int)G;
     switch (N) {
     case 16:
-        decode_kernel<T, 16, kNT><<<grid, block, 0, s>>>(H, P, G, xx, dt, A, bb, cc, D, state, yy);
+        decode_kernel<T, 16, kNT><<<grid, block, 0, s>>>(H, P, G, xx, dt, A, bb, cc, D, state, yy, prep);
         break;
     case 32:
-        decode_kernel<T, 32, kNT><<<grid, block, 0, s>>>(H, P, G, xx, dt, A, bb, cc, D, state, yy);
+        decode_kernel<T, 32, kNT><<<grid, block, 0, s>>>(H, P, G, xx, dt, A, bb, cc, D, state, yy, prep);
         break;
     case 64:
-        decode_rows_kernel<T, 64, kNT><<<grid, block, 0, s>>>(h, p, g, xx, dt, A, bb, cc, D, state, yy);
+        decode_rows_kernel<T, 64, kNT><<<grid, block, 0, s>>>(h, p, g, xx, dt, A, bb, cc, D, state, yy, prep);
         break;
     case 128:
-        decode_rows_kernel<T, 128, kNT><<<grid, block, 0, s>>>(h, p, g, xx, dt, A, bb, cc, D, state, yy);
+        decode_rows_kernel<T, 128, kNT><<<grid, block, 0, s>>>(h, p, g, xx, dt, A, bb, cc, D, state, yy, prep);
         break;
     case 256:
-        decode_rows_kernel<T, 256, kNT><<<grid, block, 0, s>>>(h, p, g, xx, dt, A, bb, cc, D, state, yy);
+        decode_rows_kernel<T, 256, kNT><<<grid, block, 0, s>>>(h, p, g, xx, dt, A, bb, cc, D, state, yy, prep);
         break;
     default:
         return hipErrorInvalidValue;
@@ -267,11 +271,11 @@ hipError_t decode_dispatch(int64_t B, int64_t H, int64_t P, int64_t N, int64_t G
 template <typename T>
 hipError_t decode_select(int64_t B, int64_t H, int64_t P, int64_t N, int64_t G, const void *x,
                          const float *dt, const float *A, const void *Bm, const void *Cm,
-                         const float *D, float *state, void *y, hipStream_t s)
+                         const float *D, float *state, void *y, DtPrep prep, hipStream_t s)
 {
     if (B * H * P * N * 4 > kNTStateBytes)
-        return decode_dispatch<T, true>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, s);
-    return decode_dispatch<T, false>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, s);
+        return decode_dispatch<T, true>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
+    return decode_dispatch<T, false>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
 }
 
 }  // namespace
@@ -296,13 +300,14 @@ hipError_t launch_state_init(float *state, const float *src, int64_t n, hipStrea
 
 hipError_t launch_decode(int bf16, int64_t B, int64_t H, int64_t P, int64_t N, int64_t G,
                          const void *x, const float *dt, const float *A, const void *Bm,
-                         const void *Cm, const float *D, float *state, void *y, hipStream_t s)
+                         const void *Cm, const float *D, float *state, void *y, DtPrep prep,
+                         hipStream_t s)
 {
     if (B * H == 0)
         return hipSuccess;
     if (bf16)
-        return decode_select<__bf16>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, s);
-    return decode_select<float>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, s);
+        return decode_select<__bf16>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
+    return decode_select<float>(B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
 }
 
 }  // namespace ssd

@@ -257,13 +257,14 @@ struct StepIn {
 template <typename T>
 constexpr int kStepsMinWaves = sizeof(T) == 2 ? 3 : 1;
 
-template <typename T, int N, int CPL, int R>
+// kSp: the dt inputs hold u and the step size is softplus(u + bias[h]).
+template <typename T, int N, int CPL, int R, bool kSp>
 __global__ __attribute__((amdgpu_flat_work_group_size(1, kStepsThreads),
                           amdgpu_waves_per_eu(kStepsMinWaves<T>))) void decode_steps_kernel(
     int S, int Bn, int H, int P, int G, int wpb, const T *__restrict__ x,
     const float *__restrict__ dt, const float *__restrict__ A, const T *__restrict__ Bm,
     const T *__restrict__ Cm, const float *__restrict__ D, float *__restrict__ state,
-    T *__restrict__ y)
+    T *__restrict__ y, const float *__restrict__ dt_bias)
 {
     using Gm = StepsGeom<N, CPL, R>;
     constexpr int esz = (int)sizeof(T);
@@ -279,6 +280,7 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kStepsThreads),
     const int rbase = p0 + grp * R;               // first state row of the lane's group
     const int myrow = rbase + (lr >> Gm::SHIFT);  // row whose y this lane holds
     const float Ah = A[h], Dh = D[h];
+    const float dtb = kSp && dt_bias ? dt_bias[h] : 0.f;
 
     // the lane's R x CPL state elements, loaded once
     float st[R][CPL];
@@ -349,7 +351,9 @@ __global__ __attribute__((amdgpu_flat_work_group_size(1, kStepsThreads),
     T *yp = yb;   // y of the step being computed
     auto step = [&](const StepIn<T, CPL> &in) {
         const float xv = elem<T, 1>(in.x, 0);
-        const float d = elem<float, 1>(in.dt, 0);
+        float d = elem<float, 1>(in.dt, 0);
+        if constexpr (kSp)
+            d = softplus_dt(d, dtb);
         const float alpha = __expf(d * Ah);
         float ux = d * xv, scn = 1.f;
         if constexpr (kLazy) {
@@ -445,7 +449,7 @@ constexpr int kSmallBatchWaves = 2048;
 template <typename T, int N, int CPL, int R>
 hipError_t launch_steps(int64_t S, int64_t B, int64_t H, int64_t P, int64_t G, const void *x,
                         const float *dt, const float *A, const void *Bm, const void *Cm,
-                        const float *D, float *state, void *y, hipStream_t s)
+                        const float *D, float *state, void *y, DtPrep prep, hipStream_t s)
 {
     using Gm = StepsGeom<N, CPL, R>;
     const int64_t wpb = (P + Gm::ROWS - 1) / Gm::ROWS;
@@ -453,35 +457,44 @@ hipError_t launch_steps(int64_t S, int64_t B, int64_t H, int64_t P, int64_t G, c
     if (waves > INT32_MAX - 4)
         return hipErrorInvalidValue;
     const int64_t blocks = (waves + kStepsThreads / 64 - 1) / (kStepsThreads / 64);
-    decode_steps_kernel<T, N, CPL, R><<<(unsigned)blocks, kStepsThreads, 0, s>>>(
-        (int)S, (int)B, (int)H, (int)P, (int)G, (int)wpb, static_cast<const T *>(x), dt, A,
-        static_cast<const T *>(Bm), static_cast<const T *>(Cm), D, state, static_cast<T *>(y));
+    if (prep.softplus)
+        decode_steps_kernel<T, N, CPL, R, true><<<(unsigned)blocks, kStepsThreads, 0, s>>>(
+            (int)S, (int)B, (int)H, (int)P, (int)G, (int)wpb, static_cast<const T *>(x), dt, A,
+            static_cast<const T *>(Bm), static_cast<const T *>(Cm), D, state,
+            static_cast<T *>(y), prep.bias);
+    else
+        decode_steps_kernel<T, N, CPL, R, false><<<(unsigned)blocks, kStepsThreads, 0, s>>>(
+            (int)S, (int)B, (int)H, (int)P, (int)G, (int)wpb, static_cast<const T *>(x), dt, A,
+            static_cast<const T *>(Bm), static_cast<const T *>(Cm), D, state,
+            static_cast<T *>(y), nullptr);
     return hipGetLastError();
 }
 
 template <typename T, int N, int CPL, int RBig>
 hipError_t steps_select(int64_t S, int64_t B, int64_t H, int64_t P, int64_t G, const void *x,
                         const float *dt, const float *A, const void *Bm, const void *Cm,
-                        const float *D, float *state, void *y, hipStream_t s)
+                        const float *D, float *state, void *y, DtPrep prep, hipStream_t s)
 {
     constexpr int RSmall = RBig / 4;
     const int64_t rows = StepsGeom<N, CPL, RBig>::ROWS;
     if (B * H * ((P + rows - 1) / rows) < kSmallBatchWaves)
-        return launch_steps<T, N, CPL, RSmall>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    return launch_steps<T, N, CPL, RBig>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+        return launch_steps<T, N, CPL, RSmall>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y,
+                                               prep, s);
+    return launch_steps<T, N, CPL, RBig>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
 }
 
 template <typename T>
 hipError_t steps_dispatch(int64_t S, int64_t B, int64_t H, int64_t P, int64_t N, int64_t G,
                           const void *x, const float *dt, const float *A, const void *Bm,
-                          const void *Cm, const float *D, float *state, void *y, hipStream_t s)
+                          const void *Cm, const float *D, float *state, void *y, DtPrep prep,
+                          hipStream_t s)
 {
     switch (N) {
-    case 16: return steps_select<T, 16, 1, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 32: return steps_select<T, 32, 2, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 64: return steps_select<T, 64, 4, 8>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 128: return steps_select<T, 128, 8, 4>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
-    case 256: return steps_select<T, 256, 4, 8>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, s);
+    case 16: return steps_select<T, 16, 1, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
+    case 32: return steps_select<T, 32, 2, 16>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
+    case 64: return steps_select<T, 64, 4, 8>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
+    case 128: return steps_select<T, 128, 8, 4>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
+    case 256: return steps_select<T, 256, 4, 8>(S, B, H, P, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
     default: return hipErrorInvalidValue;
     }
 }
@@ -491,13 +504,13 @@ hipError_t steps_dispatch(int64_t S, int64_t B, int64_t H, int64_t P, int64_t N,
 hipError_t launch_decode_steps(int bf16, int64_t S, int64_t B, int64_t H, int64_t P, int64_t N,
                                int64_t G, const void *x, const float *dt, const float *A,
                                const void *Bm, const void *Cm, const float *D, float *state,
-                               void *y, hipStream_t s)
+                               void *y, DtPrep prep, hipStream_t s)
 {
     if (S == 0 || B * H == 0)
         return hipSuccess;
     if (bf16)
-        return steps_dispatch<__bf16>(S, B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, s);
-    return steps_dispatch<float>(S, B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, s);
+        return steps_dispatch<__bf16>(S, B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
+    return steps_dispatch<float>(S, B, H, P, N, G, x, dt, A, Bm, Cm, D, state, y, prep, s);
 }
 
 }  // namespace ssd

@@ -21,26 +21,49 @@ struct EventLog {
 hipError_t log_begin(EventLog *log, hipStream_t s);
 hipError_t log_kernel(EventLog *log, const char *name, hipStream_t s);
 
+// Step-size prep fused into the kernels: with softplus set, the dt argument
+// holds u and the step size of head h is softplus(u + bias[h]) (bias NULL: 0),
+// evaluated in fp32 as max(v, 0) + log1p(exp(-|v|)), which neither overflows
+// for large v nor loses the small values of very negative v.  log1p(e) is
+// log(1 + e) * e / ((1 + e) - 1), which cancels the rounding of 1 + e (D.
+// Goldberg, "What every computer scientist should know about floating-point
+// arithmetic", 1991, theorem 4), on the hardware exp2 / log2: a few ulp.
+// Positions past the end of a sequence keep a step size of 0.
+struct DtPrep {
+    const float *bias;
+    int softplus;
+};
+
+__device__ __forceinline__ float softplus_dt(float u, float bias)
+{
+    const float v = u + bias;
+    const float e = __expf(-fabsf(v));   // (0, 1]
+    const float w = 1.f + e;
+    const float l = w == 1.f ? e : __logf(w) * (e * __builtin_amdgcn_rcpf(w - 1.f));
+    return fmaxf(v, 0.f) + l;
+}
+
 // state[i] = src ? src[i] : 0 for i < n (fill/copy kernel, graph-capturable).
 hipError_t launch_state_init(float *state, const float *src, int64_t n, hipStream_t s);
 
 // One decode step over B*H (batch row, head) pairs; io is bf16 when bf16 != 0.
 hipError_t launch_decode(int bf16, int64_t B, int64_t H, int64_t P, int64_t N, int64_t G,
                          const void *x, const float *dt, const float *A, const void *Bm,
-                         const void *Cm, const float *D, float *state, void *y, hipStream_t s);
+                         const void *Cm, const float *D, float *state, void *y, DtPrep prep,
+                         hipStream_t s);
 
 // S consecutive decode steps in one launch (state kept in registers across
 // them); x, y [S, B, H, P], dt [S, B, H], B/C [S, B, G, N].
 hipError_t launch_decode_steps(int bf16, int64_t S, int64_t B, int64_t H, int64_t P, int64_t N,
                                int64_t G, const void *x, const float *dt, const float *A,
                                const void *Bm, const void *Cm, const float *D, float *state,
-                               void *y, hipStream_t s);
+                               void *y, DtPrep prep, hipStream_t s);
 
 // fp32 chunked scan (VALU), P <= 64, N <= 128, Q <= 256.
 hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                            int64_t Q, const float *x, const float *dt, const float *A,
                            const float *Bm, const float *Cm, const float *D, const float *init,
-                           float *y, float *fin, hipStream_t s, EventLog *log);
+                           float *y, float *fin, DtPrep prep, hipStream_t s, EventLog *log);
 
 // bf16 MFMA chunked scan, P = 64, N = 128, Q % 64 == 0, Q <= 512.
 // The workspace holds the segment states and their decays.
@@ -61,6 +84,7 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q);
 hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
                             int64_t Q, const void *x, const float *dt, const float *A,
                             const void *Bm, const void *Cm, const float *D, const float *init,
-                            void *y, float *fin, void *ws, hipStream_t s, EventLog *log);
+                            void *y, float *fin, void *ws, DtPrep prep, hipStream_t s,
+                            EventLog *log);
 
 }  // namespace ssd

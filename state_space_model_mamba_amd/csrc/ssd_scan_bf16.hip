@@ -128,6 +128,7 @@ struct SegArgs {
     int nseg_launch;     // segments (scan kernel) or units (state kernel) this launch covers
     int nslot;           // units of segments 0 .. nseg-2, then the spare slot
     int seg0_from_ws;    // segment 0 reads its entering state from slot nseg-1
+    const float *dt_bias;  // step-size prep (kSp kernels): dt = softplus(u + dt_bias[h])
 };
 
 __device__ __forceinline__ f32x4 mfma32(bf16x8 a, bf16x8 b, f32x4 c)
@@ -477,10 +478,10 @@ __device__ __forceinline__ void state_update(f32x4 (&Z)[8][2], const unsigned ch
 // a_t = dt_t A_h over its 64 tokens (lane = token), in log2 units.  Updates ls
 // (and lsum, the segment's total log2 decay) and returns how the tile treats
 // the state.
-template <int kH>
+template <int kH, bool kSp>
 __device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &pf,
                                                int slot, int64_t t0, int64_t L, float Ah2,
-                                               float &ls, float &lsum, int tid)
+                                               float dtb, float &ls, float &lsum, int tid)
 {
     constexpr int kPer = Geom<kH>::kBPer, kRows = Geom<kH>::kThreads / 16;
     const int w = wave_id(), l = tid & 63, pt = tid & 127;
@@ -497,7 +498,9 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &p
         *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow +
                                    (((pt & 7) ^ xswz(row)) << 4)) = pf.x[r];
     }
-    const float dtl = pf.dt;
+    float dtl = pf.dt;
+    if constexpr (kSp)   // the step size from u; tokens past the end keep 0
+        dtl = l < L - t0 ? softplus_dt(dtl, dtb) : 0.f;
     const float lam = wave_inclusive_sum(dtl * Ah2, l);
     // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
     // hold the same sum only up to the summation order, which matters when
@@ -518,7 +521,7 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &p
 
 // The scan kernel: y of segment `seg` from the state entering it and, for the
 // last segment, the final state.
-template <int kH>
+template <int kH, bool kSp>
 __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
 {
     constexpr int kHeads = kH, kWaves = 2 * kH;
@@ -540,6 +543,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
     const int64_t tseg0 = (int64_t)seg * a.seg_tokens;
     const int64_t tseg1 = std::min<int64_t>(L, tseg0 + a.seg_tokens);
     const float Ah2 = a.A[h] * kLog2e;
+    const float dtb = kSp && a.dt_bias ? a.dt_bias[h] : 0.f;
     const float Dh = a.D[h];
     const f32x4 zero4 = {0.f, 0.f, 0.f, 0.f};
 
@@ -771,7 +775,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
     // it leaves ls unchanged, so every iteration stages without a branch
     // (which lets the compiler interleave the staging with the update).
     load_tile<kH>(pf, io, tseg0, tseg1, tid);
-    TileMode mnext = stage_tile<kH>(sm, pf, 0, tseg0, tseg1, Ah2, ls, lsum, tid);
+    TileMode mnext = stage_tile<kH, kSp>(sm, pf, 0, tseg0, tseg1, Ah2, dtb, ls, lsum, tid);
     int slot = 0;
     for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
         lds_barrier();
@@ -781,7 +785,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
         load_tile<kH, 1>(pf, io, t0 + kT, tseg1, tid);
         compute_tile(slot, md, t0);
         slot ^= 1;
-        mnext = stage_tile<kH>(sm, pf, slot, t0 + kT, tseg1, Ah2, ls, lsum, tid);
+        mnext = stage_tile<kH, kSp>(sm, pf, slot, t0 + kT, tseg1, Ah2, dtb, ls, lsum, tid);
     }
 
     if (!active || seg != a.nseg - 1)
@@ -888,6 +892,7 @@ template <int n> __device__ __forceinline__ void wait_vmcnt()
     __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (0x7 << 4) | (0xf << 8));
 }
 
+template <bool kSp>
 __global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
 {
     __shared__ __align__(16) unsigned char sB0[kT * kBRow], sB1[kT * kBRow], sB2[kT * kBRow];
@@ -914,6 +919,7 @@ __global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
     const int64_t tseg0 = sbeg + (int64_t)(unit % a.nsub) * a.unit_tokens;
     const int64_t tseg1 = std::min<int64_t>(std::min<int64_t>(L, sbeg + a.seg_tokens), tseg0 + a.unit_tokens);
     const float Ah2 = a.A[h] * kLog2e;
+    const float dtb = kSp && a.dt_bias ? a.dt_bias[h] : 0.f;
     const int zoff = (32 * ph + c) * kN + 4 * g;          // + 16 q kN + 16 nb
 
     if (unit == 0 && a.seg0_from_ws && active) {
@@ -986,7 +992,9 @@ __global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
         lds_barrier();                            // ... and every wave's; slot of t0 - kT free
         st_issue(io, Bn, Xn, Dn, t0 + 2 * kT, tseg1, w);
         const unsigned char *Bs = lds_ptr(aB), *Xs = lds_ptr(aX), *Ds = lds_ptr(aD);
-        const float dtc = reinterpret_cast<const float *>(Ds)[l];
+        float dtc = reinterpret_cast<const float *>(Ds)[l];
+        if constexpr (kSp)   // the step size from u; tokens past the end keep 0
+            dtc = l < tseg1 - t0 ? softplus_dt(dtc, dtb) : 0.f;
         const float lam = wave_inclusive_sum(dtc * Ah2, l);
         const int last = (int)std::min<int64_t>(std::max<int64_t>(tseg1 - t0, 1), kT) - 1;
         float bias;
@@ -1032,10 +1040,12 @@ __global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
 }
 
 // Scan kernel: y of every segment from its entering state, and the final state.
+// kSp: the dt input holds u and the step size is softplus(u + dt_bias[h]).
+template <bool kSp>
 __global__ __launch_bounds__(Geom<kScanHeads>::kThreads, 1) void chunk_scan_kernel(SegArgs a)
 {
     __shared__ ScanSmem<kScanHeads> sm;
-    scan_body<kScanHeads>(a, sm);
+    scan_body<kScanHeads, kSp>(a, sm);
 }
 
 int64_t env_int(const char *name, int64_t dflt)
@@ -1125,13 +1135,15 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
 hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
                             int64_t Q, const void *x, const float *dt, const float *A,
                             const void *Bm, const void *Cm, const float *D, const float *init,
-                            void *y, float *fin, void *ws, hipStream_t s, EventLog *log)
+                            void *y, float *fin, void *ws, DtPrep prep, hipStream_t s,
+                            EventLog *log)
 {
     if (B * H == 0 || L == 0)
         return hipSuccess;
     SegArgs a{};
     a.x = static_cast<const __bf16 *>(x);
     a.dt = dt;
+    a.dt_bias = prep.bias;
     a.A = A;
     a.B = static_cast<const __bf16 *>(Bm);
     a.C = static_cast<const __bf16 *>(Cm);
@@ -1161,13 +1173,21 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     if (plan.nseg > 1) {
         a.nq = nq1;
         a.nseg_launch = (a.nseg - 1) * a.nsub;
-        seg_state_kernel<<<(unsigned)(B * G * nq1 * a.nseg_launch), kStThreads, 0, s>>>(a);
+        const unsigned grid = (unsigned)(B * G * nq1 * a.nseg_launch);
+        if (prep.softplus)
+            seg_state_kernel<true><<<grid, kStThreads, 0, s>>>(a);
+        else
+            seg_state_kernel<false><<<grid, kStThreads, 0, s>>>(a);
         if ((e = hipGetLastError()) != hipSuccess || (e = log_kernel(log, "seg_state_kernel", s)) != hipSuccess)
             return e;
     }
     a.nq = nq3;
     a.nseg_launch = a.nseg;
-    chunk_scan_kernel<<<(unsigned)(B * G * nq3 * plan.nseg), Geom<kScanHeads>::kThreads, 0, s>>>(a);
+    const unsigned grid = (unsigned)(B * G * nq3 * plan.nseg);
+    if (prep.softplus)
+        chunk_scan_kernel<true><<<grid, Geom<kScanHeads>::kThreads, 0, s>>>(a);
+    else
+        chunk_scan_kernel<false><<<grid, Geom<kScanHeads>::kThreads, 0, s>>>(a);
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return log_kernel(log, "chunk_scan_kernel", s);

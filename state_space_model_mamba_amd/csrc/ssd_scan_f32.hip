@@ -29,7 +29,7 @@ __global__ __launch_bounds__(kF32Threads) void scan_f32_kernel(
     int64_t L, int64_t H, int64_t P, int64_t N, int64_t G, int64_t Q,
     const float *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
     const float *__restrict__ Bm, const float *__restrict__ Cm, const float *__restrict__ D,
-    const float *__restrict__ init, float *__restrict__ y, float *__restrict__ fin)
+    const float *__restrict__ init, float *__restrict__ y, float *__restrict__ fin, DtPrep prep)
 {
     __shared__ float S[kF32MaxP * kF32MaxN];
     __shared__ double lam[kF32MaxQ];
@@ -40,6 +40,7 @@ __global__ __launch_bounds__(kF32Threads) void scan_f32_kernel(
     const int tid = threadIdx.x;
     const int64_t bh = blockIdx.x, b = bh / H, h = bh - b * H, g = h / (H / G);
     const float Ah = A[h], Dh = D[h];
+    const float dtb = prep.softplus && prep.bias ? prep.bias[h] : 0.f;
     const int64_t PN = P * N;
 
     for (int64_t e = tid; e < PN; e += kF32Threads)
@@ -48,8 +49,10 @@ __global__ __launch_bounds__(kF32Threads) void scan_f32_kernel(
     for (int64_t c0 = 0; c0 < L; c0 += Q) {
         const int64_t Qc = (L - c0 < Q) ? (L - c0) : Q;
         __syncthreads();
-        for (int64_t i = tid; i < Qc; i += kF32Threads)
-            dts[i] = dt[(b * L + c0 + i) * H + h];
+        for (int64_t i = tid; i < Qc; i += kF32Threads) {
+            const float u = dt[(b * L + c0 + i) * H + h];
+            dts[i] = prep.softplus ? softplus_dt(u, dtb) : u;
+        }
         __syncthreads();
         if (tid == 0) {
             double acc = 0.0;
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(kF32Threads) void scan_f32_kernel(
 hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                            int64_t Q, const float *x, const float *dt, const float *A,
                            const float *Bm, const float *Cm, const float *D, const float *init,
-                           float *y, float *fin, hipStream_t s, EventLog *log)
+                           float *y, float *fin, DtPrep prep, hipStream_t s, EventLog *log)
 {
     if (P > kF32MaxP || N > kF32MaxN || Q > kF32MaxQ)
         return hipErrorInvalidValue;
@@ -126,7 +129,7 @@ hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N
     if (e != hipSuccess)
         return e;
     scan_f32_kernel<<<(unsigned)(B * H), kF32Threads, 0, s>>>(L, H, P, N, G, Q, x, dt, A, Bm, Cm,
-                                                             D, init, y, fin);
+                                                             D, init, y, fin, prep);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;

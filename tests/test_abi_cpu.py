@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(ssd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ssd_version() == 10000
+    assert lib.ssd_version() == 10100
 
 
 def test_status_strings(lib):
@@ -69,8 +69,10 @@ def test_workspace_size_host_logic(lib):
     assert ws_size(lib, dims(seqlen=-1))[0] == 2
     assert ws_size(lib, dims(io_dtype=7))[0] == 3
     d = dims()
-    d.reserved = 1
+    d.flags = 2                                          # unknown flag bit
     assert ws_size(lib, d)[0] == 2
+    d.flags = ssd.SSD_DT_SOFTPLUS                        # the fused softplus is accepted
+    assert ws_size(lib, d)[0] == 0
     assert lib.ssd_chunk_scan_workspace_size(None, ctypes.byref(ctypes.c_size_t())) == 1
     assert lib.ssd_chunk_scan_workspace_size(ctypes.byref(dims()), None) == 1
 
@@ -163,3 +165,25 @@ def test_decode_steps_validation(lib):
                                 None) == 0
     assert lib.ssd_decode_steps(ctypes.byref(d), ctypes.c_int64(0), *([None] * 8), None) == 0
     assert lib.ssd_decode_steps(None, ctypes.c_int64(1), *([None] * 8), None) == 1
+
+
+def test_dt_bias_validation(lib):
+    """The fused step-size prep: the bias is 4-byte aligned and outside the outputs
+    (every call here fails validation, so nothing is launched)."""
+    p = lambda v: ctypes.c_void_p(v)
+    d = dims()
+    d.flags = ssd.SSD_DT_SOFTPLUS
+    d.dt_bias = FAKE + (9 << 33) + 2
+    assert scan(lib, d) == 7                              # misaligned bias
+    d.dt_bias = FAKE + (6 << 33) + 64
+    assert scan(lib, d) == 4                              # bias inside y
+    d.dt_bias = FAKE + (7 << 33) + 64
+    assert scan(lib, d) == 4                              # bias inside the final state
+    base = [p(FAKE + (k << 33)) for k in range(8)]
+    d.dt_bias = FAKE + (7 << 33) + 8                      # bias inside y of a decode step
+    assert lib.ssd_decode_step(ctypes.byref(d), *base, None) == 4
+    d.dt_bias = FAKE + (6 << 33) + 8                      # ... or inside the state
+    assert lib.ssd_decode_steps(ctypes.byref(d), ctypes.c_int64(3), *base, None) == 4
+    d.flags = 0                                           # without the flag the bias is not read
+    d.dt_bias = FAKE + (6 << 33) + 2
+    assert scan(lib, d, x=None) == 1

@@ -352,3 +352,26 @@ def test_mutants_are_caught():
             if not caught:
                 survivors.append(name)
         assert not survivors, f"mutants not caught by any pin: {survivors}"
+
+
+# ----------------------------------------------------------------------------
+# the fused step-size prep: softplus
+# ----------------------------------------------------------------------------
+def test_dt_softplus_pins():
+    """softplus(0) = ln 2; softplus(v) - softplus(-v) = v; its large- and
+    small-argument limits v and exp(v); the bias is added per head (last axis)."""
+    assert abs(oracle.dt_softplus(0.0) - math.log(2.0)) < 1e-15
+    rng = np.random.default_rng(5)
+    v = rng.uniform(-30, 30, 1000)
+    assert np.max(np.abs(oracle.dt_softplus(v) - oracle.dt_softplus(-v) - v)) < 1e-12
+    big = np.array([40.0, 100.0, 700.0, 1e5])
+    assert np.array_equal(oracle.dt_softplus(big), big)
+    small = np.array([-40.0, -100.0, -700.0])
+    assert np.allclose(oracle.dt_softplus(small), np.exp(small), rtol=1e-12, atol=0)
+    # at the workload's range the value is the step size the draw produces
+    for d in (0.001, 0.01, 0.1):
+        assert abs(oracle.dt_softplus(math.log(math.expm1(d))) - d) < 1e-15
+    u = rng.standard_normal((3, 5, 4))
+    bias = np.array([0.5, -1.0, 2.0, 0.0])
+    assert np.array_equal(oracle.dt_softplus(u, bias), oracle.dt_softplus(u + bias))
+    assert np.all(oracle.dt_softplus(u, bias) > 0)
