@@ -143,6 +143,31 @@ ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const float *dt, 
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssd_chunk_scan_varlen -- prefill of a packed batch of sequences of
+ * different lengths, each its own recurrence with its own cache (section 2 of
+ * the page, per sequence, as ssd_chunk_scan).  dims->batch = number of sequences S, dims->seqlen = total
+ * tokens T; cu_seqlens is a HOST array of S + 1 offsets (cu[0] = 0,
+ * non-decreasing, cu[S] = T): sequence i is tokens cu[i] .. cu[i+1]-1.
+ *   x [T,H,P], dt [T,H], B [T,G,N], C [T,G,N]    packed inputs (io_dtype / fp32)
+ *   A [H], D [H]                                  as for ssd_chunk_scan
+ *   initial_states [S,H,P,N] fp32 or NULL         input
+ *   y [T,H,P]                                     output
+ *   final_states [S,H,P,N] fp32                   output (may alias initial_states)
+ *   workspace : >= ssd_chunk_scan_varlen_workspace_size bytes
+ * Zero-length sequences pass their state through.  Consecutive sequences of
+ * equal length run as one batched scan, so a batch of equal lengths costs one
+ * call; every run is validated before the first is enqueued.  Supported shapes
+ * and the alignment of each sequence's slices as for ssd_chunk_scan.
+ */
+ssd_status ssd_chunk_scan_varlen_workspace_size(const ssd_dims *dims, const int64_t *cu_seqlens,
+                                                size_t *bytes);
+ssd_status ssd_chunk_scan_varlen(const ssd_dims *dims, const int64_t *cu_seqlens, const void *x,
+                                 const float *dt, const float *A, const void *B, const void *C,
+                                 const float *D, const float *initial_states, void *y,
+                                 float *final_states, void *workspace, size_t workspace_bytes,
+                                 void *stream);
+
+/*
  * ssd_decode_step -- one O(1) cached decode step for every sequence (section
  * 2 of the page: the fixed-size on-device cache, updated per generated token
  * with no host round trip; section 4: decode is bandwidth-bound).  Each

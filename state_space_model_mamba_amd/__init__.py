@@ -14,6 +14,7 @@ to pass u instead of dt; the step size is then softplus(u + dt_bias) in the kern
     ssd_decode_step(x, dt, A, B, C, D, state, y=None) -> y
     ssd_decode_steps(x, dt, A, B, C, D, state, y=None) -> y   (S steps in one launch)
     ssd_chunk_scan_timed(...) -> (y, final_state, [(kernel, ms), ...])
+    ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, ...) -> (y, final_states)
 """
 from __future__ import annotations
 
@@ -28,7 +29,8 @@ SSD_DT_SOFTPLUS = 1            # ssd_dims.flags: dt holds u, the step size is so
 STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPPORTED",
           4: "SSD_ERR_ALIAS", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_DEVICE", 7: "SSD_ERR_ALIGNMENT"}
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_state_init", "ssd_chunk_scan_workspace_size",
-           "ssd_chunk_scan", "ssd_decode_step", "ssd_decode_steps", "ssd_chunk_scan_timed")
+           "ssd_chunk_scan", "ssd_decode_step", "ssd_decode_steps", "ssd_chunk_scan_timed",
+           "ssd_chunk_scan_varlen_workspace_size", "ssd_chunk_scan_varlen")
 
 
 class SsdError(RuntimeError):
@@ -79,6 +81,11 @@ def load(path: str | None = None):
     lib.ssd_decode_step.restype = ctypes.c_int
     lib.ssd_decode_steps.argtypes = [dims, ctypes.c_int64] + [vp] * 9
     lib.ssd_decode_steps.restype = ctypes.c_int
+    cu = ctypes.POINTER(ctypes.c_int64)
+    lib.ssd_chunk_scan_varlen_workspace_size.argtypes = [dims, cu, i64p]
+    lib.ssd_chunk_scan_varlen_workspace_size.restype = ctypes.c_int
+    lib.ssd_chunk_scan_varlen.argtypes = [dims, cu] + [vp] * 10 + [ctypes.c_size_t, vp]
+    lib.ssd_chunk_scan_varlen.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -208,3 +215,47 @@ def ssd_decode_steps(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=
         ctypes.byref(d), ctypes.c_int64(nsteps), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
         _ptr(D), _ptr(state), _ptr(y), _stream(stream)))
     return y
+
+
+def _cu_array(cu_seqlens):
+    import numpy as np
+    cu = np.ascontiguousarray(np.asarray(cu_seqlens, dtype=np.int64))
+    return cu, cu.ctypes.data_as(ctypes.POINTER(ctypes.c_int64))
+
+
+def ssd_chunk_scan_varlen_workspace_size(cu_seqlens, nheads, headdim, dstate, ngroups, chunk,
+                                         io_dtype=SSD_BF16) -> int:
+    cu, cup = _cu_array(cu_seqlens)
+    d = make_dims(len(cu) - 1, int(cu[-1]), nheads, headdim, dstate, ngroups, chunk, io_dtype)
+    n = ctypes.c_size_t(0)
+    _check("ssd_chunk_scan_varlen_workspace_size",
+           load().ssd_chunk_scan_varlen_workspace_size(ctypes.byref(d), cup, ctypes.byref(n)))
+    return int(n.value)
+
+
+def ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, initial_states=None, y=None,
+                          final_states=None, workspace=None, stream=None, dt_softplus=False,
+                          dt_bias=None):
+    """Prefill of a packed batch: x[T, H, P], dt[T, H], B/C[T, G, N]; sequence i is
+    tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (a host sequence of S + 1 offsets).
+    Returns (y[T, H, P], final_states[S, H, P, N])."""
+    import torch
+    T, H, P = x.shape
+    G, N = B.shape[1], B.shape[2]
+    cu, cup = _cu_array(cu_seqlens)
+    nseq = len(cu) - 1
+    io = _io_dtype(x)
+    d = make_dims(nseq, T, H, P, N, G, chunk, io, dt_softplus, dt_bias)
+    if y is None:
+        y = torch.empty_like(x)
+    if final_states is None:
+        final_states = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device)
+    need = ssd_chunk_scan_varlen_workspace_size(cu, H, P, N, G, chunk, io)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("ssd_chunk_scan_varlen", load().ssd_chunk_scan_varlen(
+        ctypes.byref(d), cup, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+        _ptr(initial_states), _ptr(y), _ptr(final_states), _ptr(workspace), ws_bytes,
+        _stream(stream)))
+    return y, final_states

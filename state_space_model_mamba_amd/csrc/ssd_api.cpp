@@ -2,6 +2,7 @@
 // kernels.  The contract of every entry point is documented in include/ssd.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "ssd.h"
@@ -137,9 +138,11 @@ size_t scan_workspace(const ssd_dims *d)
     return ssd::plan_scan_bf16(d->batch, d->seqlen, d->nheads, d->ngroups, d->chunk).ws_bytes;
 }
 
+// Validates a scan call and, when `launch`, enqueues it.
 ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const float *A,
                     const void *B, const void *C, const float *D, const float *init, void *y,
-                    float *fin, void *ws, size_t ws_bytes, hipStream_t s, ssd::EventLog *log)
+                    float *fin, void *ws, size_t ws_bytes, hipStream_t s, ssd::EventLog *log,
+                    bool launch = true)
 {
     ssd_status st = check_dims(d, true);
     if (st != SSD_OK)
@@ -161,6 +164,8 @@ ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const flo
         return SSD_ERR_ALIAS;
     if (L == 0) {
         // no tokens: the cache is handed through unchanged
+        if (!launch)
+            return SSD_OK;
         return device_status(ssd::launch_state_init(fin, init, Bn * H * P * N, s));
     }
     if (!x || !dt || !A || !B || !C || !D || !y)
@@ -192,6 +197,8 @@ ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const flo
     const Span outs[] = {sy, sfin, sws};
     if ((st = check_dt_bias(d, outs, 3)) != SSD_OK)
         return st;
+    if (!launch)
+        return SSD_OK;
 
     hipError_t e;
     if (d->io_dtype == SSD_BF16) {
@@ -205,6 +212,51 @@ ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const flo
                                  static_cast<float *>(y), fin, dt_prep(d), s, log);
     }
     return device_status(e);
+}
+
+// Packed variable-length batches: sequence i holds tokens cu[i] .. cu[i+1]-1
+// of the [T, ...] inputs.  Consecutive sequences of equal length are laid out
+// exactly like a [b, L, ...] batch, so each such run is one scan call.
+ssd_status varlen_check(const ssd_dims *d, const int64_t *cu)
+{
+    if (!d || !cu)
+        return SSD_ERR_NULL;
+    if (d->batch < 0 || d->seqlen < 0)
+        return SSD_ERR_SHAPE;
+    if (cu[0] != 0 || cu[d->batch] != d->seqlen)
+        return SSD_ERR_SHAPE;
+    for (int64_t i = 0; i < d->batch; ++i)
+        if (cu[i + 1] < cu[i])
+            return SSD_ERR_SHAPE;
+    ssd_dims one = *d;   // the packed token arrays as one sequence of T tokens
+    one.batch = 1;
+    ssd_status st = check_dims(&one, true);
+    if (st != SSD_OK)
+        return st;
+    ssd_dims seqs = *d;  // the per-sequence states
+    seqs.seqlen = 0;
+    if ((st = check_dims(&seqs, true)) != SSD_OK)
+        return st;
+    return scan_supported(d);
+}
+
+template <class F>
+ssd_status for_each_run(const ssd_dims *d, const int64_t *cu, F f)
+{
+    for (int64_t i = 0; i < d->batch;) {
+        const int64_t len = cu[i + 1] - cu[i];
+        int64_t j = i + 1;
+        while (j < d->batch && cu[j + 1] - cu[j] == len)
+            ++j;
+        ssd_dims r = *d;
+        r.batch = j - i;
+        r.seqlen = len;
+        const ssd_status st = f(r, i, cu[i]);
+        if (st != SSD_OK)
+            return st;
+        i = j;
+    }
+    return SSD_OK;
 }
 
 }  // namespace
@@ -397,4 +449,73 @@ SSD_EXPORT ssd_status ssd_decode_steps(const ssd_dims *dims, int64_t nsteps, con
     return device_status(ssd::launch_decode_steps(dims->io_dtype == SSD_BF16, nsteps, Bn, H, P,
                                                   N, G, x, dt, A, B, C, D, state, y,
                                                   dt_prep(dims), static_cast<hipStream_t>(stream)));
+}
+
+SSD_EXPORT ssd_status ssd_chunk_scan_varlen_workspace_size(const ssd_dims *dims,
+                                                           const int64_t *cu_seqlens,
+                                                           size_t *bytes)
+{
+    ssd_status st = varlen_check(dims, cu_seqlens);
+    if (st != SSD_OK)
+        return st;
+    if (!bytes)
+        return SSD_ERR_NULL;
+    size_t need = 0;
+    for_each_run(dims, cu_seqlens, [&](const ssd_dims &r, int64_t, int64_t) {
+        need = std::max(need, scan_workspace(&r));
+        return SSD_OK;
+    });
+    *bytes = need;
+    return SSD_OK;
+}
+
+SSD_EXPORT ssd_status ssd_chunk_scan_varlen(const ssd_dims *dims, const int64_t *cu_seqlens,
+                                            const void *x, const float *dt, const float *A,
+                                            const void *B, const void *C, const float *D,
+                                            const float *initial_states, void *y,
+                                            float *final_states, void *workspace,
+                                            size_t workspace_bytes, void *stream)
+{
+    ssd_status st = varlen_check(dims, cu_seqlens);
+    if (st != SSD_OK)
+        return st;
+    if (dims->batch == 0)
+        return SSD_OK;
+    if (!final_states)
+        return SSD_ERR_NULL;
+    const int64_t esz = dims->io_dtype == SSD_BF16 ? 2 : 4;
+    const int64_t T = dims->seqlen, H = dims->nheads, P = dims->headdim, N = dims->dstate,
+                  G = dims->ngroups, HPN = H * P * N;
+    // whole buffers: no output may overlap an input of another sequence either
+    const Span sy = span(y, T * H * P * esz), sfin = span(final_states, dims->batch * HPN * 4);
+    const Span sinit = span(initial_states, dims->batch * HPN * 4);
+    const Span sws = span(workspace, (int64_t)workspace_bytes);
+    const Span ins[] = {span(x, T * H * P * esz), span(dt, T * H * 4), span(A, H * 4),
+                        span(B, T * G * N * esz), span(C, T * G * N * esz), span(D, H * 4)};
+    for (const Span &in : ins)
+        if (overlap(sy, in) || overlap(sfin, in) || overlap(sws, in))
+            return SSD_ERR_ALIAS;
+    if (overlap(sy, sfin) || overlap(sy, sinit) || overlap(sy, sws) || overlap(sws, sfin) ||
+        overlap(sws, sinit))
+        return SSD_ERR_ALIAS;
+    if (initial_states && initial_states != final_states && overlap(sfin, sinit))
+        return SSD_ERR_ALIAS;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    auto call = [&](bool launch) {
+        return for_each_run(dims, cu_seqlens, [&](const ssd_dims &r, int64_t seq, int64_t tok) {
+            const char *xb = static_cast<const char *>(x), *bb = static_cast<const char *>(B),
+                       *cb = static_cast<const char *>(C);
+            char *yb = static_cast<char *>(y);
+            return run_scan(&r, xb ? xb + tok * H * P * esz : nullptr, dt ? dt + tok * H : nullptr,
+                            A, bb ? bb + tok * G * N * esz : nullptr,
+                            cb ? cb + tok * G * N * esz : nullptr, D,
+                            initial_states ? initial_states + seq * HPN : nullptr,
+                            yb ? yb + tok * H * P * esz : nullptr, final_states + seq * HPN,
+                            workspace, workspace_bytes, s, nullptr, launch);
+        });
+    };
+    // every run is validated before the first is enqueued
+    if ((st = call(false)) != SSD_OK)
+        return st;
+    return call(true);
 }

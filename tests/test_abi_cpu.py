@@ -187,3 +187,43 @@ def test_dt_bias_validation(lib):
     d.flags = 0                                           # without the flag the bias is not read
     d.dt_bias = FAKE + (6 << 33) + 2
     assert scan(lib, d, x=None) == 1
+
+
+def test_varlen_host_logic(lib):
+    """Packed variable-length batches: offsets are validated and the workspace is
+    the largest of the equal-length runs' (CPU only, nothing launched)."""
+    H, P, N, G, Q = 80, 64, 128, 1, 256
+
+    def size(cu):
+        arr = (ctypes.c_int64 * len(cu))(*cu)
+        d = dims(batch=len(cu) - 1, seqlen=cu[-1], nheads=H, headdim=P, dstate=N, ngroups=G,
+                 chunk=Q)
+        n = ctypes.c_size_t(0)
+        return lib.ssd_chunk_scan_varlen_workspace_size(ctypes.byref(d), arr, ctypes.byref(n)), n.value
+
+    def run_ws(b, L):
+        return ws_size(lib, dims(batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G,
+                                 chunk=Q))[1]
+
+    rc, n = size([0, 8192, 8192 + 100, 8192 + 200, 8192 + 4296])
+    assert rc == 0 and n == max(run_ws(1, 8192), run_ws(2, 100), run_ws(1, 4096))
+    assert size([0, 4096, 8192, 12288, 16384]) == (0, run_ws(4, 4096))   # one run
+    assert size([0, 0, 0])[0] == 0
+    assert size([1, 5])[0] == 2                # cu[0] != 0
+    assert size([0, 7, 5, 9])[0] == 2          # decreasing
+    arr = (ctypes.c_int64 * 3)(0, 5, 9)
+    d = dims(batch=2, seqlen=10)               # cu[S] != T
+    assert lib.ssd_chunk_scan_varlen_workspace_size(ctypes.byref(d), arr,
+                                                    ctypes.byref(ctypes.c_size_t())) == 2
+    assert lib.ssd_chunk_scan_varlen_workspace_size(ctypes.byref(d), None,
+                                                    ctypes.byref(ctypes.c_size_t())) == 1
+    # a scan whose last run has a misaligned slice fails before anything is launched:
+    # fp32 I/O with H = 5, P = 3 is 60 bytes of x per token; lengths 4, 5, 6 are three
+    # runs starting at tokens 0, 4, 9, i.e. bytes 0, 240 (16-aligned) and 540 (not)
+    arr = (ctypes.c_int64 * 4)(0, 4, 9, 15)
+    d = dims(batch=3, seqlen=15, nheads=5, headdim=3, dstate=16, ngroups=1, chunk=64,
+             io_dtype=ssd.SSD_F32)
+    p = lambda v: ctypes.c_void_p(v)
+    rc = lib.ssd_chunk_scan_varlen(ctypes.byref(d), arr, *[p(FAKE + (k << 33)) for k in range(6)],
+                                   None, p(FAKE + (6 << 33)), p(FAKE + (7 << 33)), None, 0, None)
+    assert rc == 7
