@@ -318,6 +318,55 @@ def bench_decode(args):
     return w, out
 
 
+VARLEN_LENGTHS = (8192, 6144, 4096, 4096, 2048, 1024, 512, 512)
+
+
+def bench_varlen(args):
+    """A continuous-batching prefill: prompts of mixed lengths packed into one
+    ssd_chunk_scan_varlen call at the 2.7B head shape (80 x 64, dstate 128,
+    chunk 256, bf16)."""
+    import torch
+
+    import ssd_inputs as si
+    import state_space_model_mamba_amd as ssd
+
+    T = sum(VARLEN_LENGTHS)
+    w = si.small_workload(batch=1, seqlen=T, nheads=80, headdim=64, dstate=128, ngroups=1,
+                          chunk=256, seed=211)
+    A, D = si.head_params(w)
+    inp = si.prefill_inputs(w)
+    x, dt = to_dev(inp["x"][0], True), to_dev(inp["dt"][0])
+    B, C = to_dev(inp["B"][0], True), to_dev(inp["C"][0], True)
+    dA, dD = to_dev(A), to_dev(D)
+    del inp
+    cu = np.concatenate([[0], np.cumsum(VARLEN_LENGTHS)]).astype(np.int64)
+    y = torch.empty_like(x)
+    fs = torch.empty((len(VARLEN_LENGTHS), 80, 64, 128), dtype=torch.float32, device="cuda")
+    nws = ssd.ssd_chunk_scan_varlen_workspace_size(cu, 80, 64, 128, 1, 256)
+    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        ssd.ssd_chunk_scan_varlen(x, dt, dA, B, C, dD, cu, 256, y=y, final_states=fs, workspace=ws)
+
+    for _ in range(3):
+        step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / args.steps
+    runs = sum(1 for i in range(len(VARLEN_LENGTHS))
+               if i == 0 or VARLEN_LENGTHS[i] != VARLEN_LENGTHS[i - 1])
+    return {"workload": f"ssd_chunk_scan_varlen, {len(VARLEN_LENGTHS)} packed sequences of "
+                        f"lengths {list(VARLEN_LENGTHS)} ({T} tokens), 80 heads x 64, dstate 128, "
+                        f"chunk 256, bf16",
+            "event_ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
+            "scan_calls": runs}
+
+
 def cpu_baseline_prefill(w, npairs=None):
     """The fp64 oracle on `npairs` of the layer's (batch, head) sequences, full
     length each, threaded over pairs; tokens/s scaled to the whole layer."""
@@ -443,6 +492,7 @@ def main():
             "note": "the same prefill with dt passed as u and softplus(u + dt_bias) formed "
                     "inside the scan kernels (ssd_dims.flags = SSD_DT_SOFTPLUS)"},
     }
+    line["prefill_varlen"] = bench_varlen(args)
     if not args.no_decode:
         wd, dec = bench_decode(args)
         main_b = max(dec)
