@@ -202,17 +202,17 @@ def bench_prefill(args):
     # the same step with the fused step-size prep (dt read as u, softplus(u + bias)
     # formed in the kernels); u and the bias are arbitrary here, only time matters
     bias = torch.zeros(w.nheads, dtype=torch.float32, device="cuda")
-    for _ in range(3):
+    for _ in range(0 if args.no_extras else 3):
         ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
                            dt_softplus=True, dt_bias=bias)
     torch.cuda.synchronize()
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(0 if args.no_extras else args.steps):
         ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
                            dt_softplus=True, dt_bias=bias)
     e1.record()
     torch.cuda.synchronize()
-    sp_ms = e0.elapsed_time(e1) / args.steps
+    sp_ms = None if args.no_extras else e0.elapsed_time(e1) / args.steps
     nbytes = prefill_bytes(w)
     flops = prefill_useful_flops(w)
     k3 = kern["chunk_scan_kernel"]
@@ -435,6 +435,9 @@ def main():
     ap.add_argument("--decode-batches", type=str, default="256,64,16,1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the fused-softplus and mixed-length prefill timings (counter runs: "
+                         "every dispatch of a kernel is then the main workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
@@ -492,7 +495,8 @@ def main():
             "note": "the same prefill with dt passed as u and softplus(u + dt_bias) formed "
                     "inside the scan kernels (ssd_dims.flags = SSD_DT_SOFTPLUS)"},
     }
-    line["prefill_varlen"] = bench_varlen(args)
+    if not args.no_extras:
+        line["prefill_varlen"] = bench_varlen(args)
     if not args.no_decode:
         wd, dec = bench_decode(args)
         main_b = max(dec)
