@@ -41,7 +41,8 @@ FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s (256 CU x 2.4 GHz x
 METRIC = "SSD prefill tokens/s (MFMA %) + decode steps/s (HBM GB/s %) at 2.7B-layer shape"
 KERNEL_SOURCES = ["state_space_model_mamba_amd/csrc/ssd_scan_bf16.hip",
                   "state_space_model_mamba_amd/csrc/ssd_decode.hip",
-                  "state_space_model_mamba_amd/csrc/ssd_decode_steps.hip"]
+                  "state_space_model_mamba_amd/csrc/ssd_decode_steps.hip",
+                  "state_space_model_mamba_amd/csrc/ssd_gdn.hip"]
 
 
 def prefill_bytes(w) -> int:
@@ -118,7 +119,8 @@ def _counter_means(path, counter):
             copy += v
         short = name.split("(")[0].split("::")[-1]
         for k in ("seg_state_kernel", "chunk_scan_kernel", "decode_rows_kernel",
-                  "decode_steps_kernel", "decode_kernel", "scan_f32_kernel"):
+                  "decode_steps_kernel", "gdn_decode_kernel", "decode_kernel",
+                  "scan_f32_kernel"):
             if k in short or k in name:
                 per.setdefault(k, []).append(v)
                 break
@@ -316,6 +318,78 @@ def bench_decode(args):
         del x, dt, B, C, y, state
         torch.cuda.empty_cache()
     return w, out
+
+
+def gdn_bytes(b, sh, esz=2) -> int:
+    """HBM bytes of one GDN decode step: the state read and written once, q, k, v, o, g, beta."""
+    state = b * sh["v_heads"] * sh["dk"] * sh["dv"] * 4
+    return (2 * state + 2 * b * sh["qk_heads"] * sh["dk"] * esz + 2 * b * sh["v_heads"] * sh["dv"] * esz
+            + 2 * b * sh["v_heads"] * 4)
+
+
+def bench_gdn(args):
+    """Gated DeltaNet decode (ssd_gdn_decode_step) at the FPGA page's shape: 32 value
+    heads over 16 query/key heads, 128 x 128 fp32 state per value head, bf16 q/k/v/o;
+    consecutive in-place steps with fresh tokens, eager and graph-replayed."""
+    import torch
+
+    import ssd_inputs as si
+    import state_space_model_mamba_amd as ssd
+
+    sh = si.GDN_SHAPE
+    out = {}
+    for b in (256, 1):
+        steps = 200
+        tok = si.gdn_tokens(400 + b, steps, b, sh["qk_heads"], sh["v_heads"], sh["dk"], sh["dv"])
+        q, k, v = to_dev(tok["q"], True), to_dev(tok["k"], True), to_dev(tok["v"], True)
+        g, beta = to_dev(tok["g"]), to_dev(tok["beta"])
+        state = to_dev(tok["state0"])
+        del tok
+        o = torch.empty_like(v)
+
+        def run():
+            for t in range(steps):
+                ssd.ssd_gdn_decode_step(q[t], k[t], v[t], g[t], beta[t], state, o=o[t])
+
+        run()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        run()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                run()
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gms = e0.elapsed_time(e1) / steps
+        nb = gdn_bytes(b, sh)
+        out[b] = {"event_ms_per_step": ms, "graph_ms_per_step": gms, "bytes_per_step": nb,
+                  "gbs": nb / (ms * 1e-3) / 1e9, "graph_gbs": nb / (gms * 1e-3) / 1e9}
+        del q, k, v, g, beta, state, o, graph
+        torch.cuda.empty_cache()
+    r = out[256]
+    return {"workload": "ssd_gdn_decode_step, 32 value heads over 16 query/key heads, "
+                        "128 x 128 fp32 state per value head (2 MB per sequence), bf16 q/k/v/o, "
+                        "200 consecutive in-place steps",
+            "roofline": {"bound": "hbm", "kernel": "gdn_decode_kernel", "batch": 256,
+                         "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": r["gbs"] / HBM_PEAK_GBS,
+                         "traffic": committed_traffic("gdn_decode_kernel"),
+                         "bytes_per_launch": r["bytes_per_step"],
+                         "avg_launch_ms": r["event_ms_per_step"]},
+            "batches": {str(b): v for b, v in sorted(out.items())},
+            "note": "batch 1 moves 2 MB per step (MALL-resident, launch-bound eager)"}
 
 
 VARLEN_LENGTHS = (8192, 6144, 4096, 4096, 2048, 1024, 512, 512)
@@ -535,6 +609,7 @@ def main():
                                  "tflops": r["steps_launch_tflops"]}
                         for b, r in sorted(dec.items())},
         }
+        line["gdn_decode"] = bench_gdn(args)
         if not args.no_cpu_baseline:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(wd)
             line["decode_steps"]["cpu_baseline"] = dict(

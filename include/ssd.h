@@ -207,6 +207,40 @@ ssd_status ssd_decode_steps(const ssd_dims *dims, int64_t nsteps, const void *x,
                             float *state, void *y, void *stream);
 
 /*
+ * ssd_gdn_decode_step -- one Gated DeltaNet decode step, the second
+ * fixed-state recurrence the pages treat ("A Persistent-State Dataflow
+ * Accelerator for Memory-Bound Linear Attention Decode on FPGA", section 2).
+ * Per batch row b and value head j, with query/key head i = j / (Hv / Hk)
+ * (value heads grouped onto query/key heads, section 2C):
+ *     dv  = beta[b,j] (v[b,j] - g[b,j] S^T k[b,i])
+ *     S  <- g[b,j] S + k[b,i] dv^T          (S is [dk, dv] fp32, in place)
+ *     o[b,j] = S^T q[b,i]                   (computed as g S_old^T q + (q.k) dv,
+ *                                            section 2B: one read, one write of S)
+ * The page writes the update and the output identity; dv is the gated delta
+ * rule's.
+ *   q, k  [B, Hk, dk]   io_dtype          v, o [B, Hv, dv]   io_dtype
+ *   g, beta [B, Hv]     fp32 (decay gate and write strength, taken as given)
+ *   state [B, Hv, dk, dv] fp32, updated in place
+ * o must not overlap the state or any input; the state must not overlap an
+ * input.  Alignment: state 16 bytes; q, k, v, o element-aligned; g, beta 4.
+ * Supported: dk in {64, 128, 256}, dv in {64, 128, 256}, io_dtype SSD_F32 or
+ * SSD_BF16.  B == 0 does nothing.
+ */
+typedef struct ssd_gdn_dims {
+    int64_t batch;     /* B >= 0                                              */
+    int64_t qk_heads;  /* Hk >= 1                                             */
+    int64_t v_heads;   /* Hv >= 1, Hv % Hk == 0                               */
+    int64_t dk;        /* key dimension (state rows)                          */
+    int64_t dv;        /* value dimension (state columns)                     */
+    int32_t io_dtype;  /* ssd_dtype of q, k, v, o                             */
+    int32_t reserved;  /* must be 0                                           */
+} ssd_gdn_dims;
+
+ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const void *k,
+                               const void *v, const float *g, const float *beta, float *state,
+                               void *o, void *stream);
+
+/*
  * ssd_chunk_scan_timed -- measurement entry point: the same computation as
  * ssd_chunk_scan (same arguments and results), run synchronously; the device
  * time of each kernel the scan launched is written to kernel_ms[0 ..

@@ -238,3 +238,32 @@ def small_workload(name="small", batch=2, seqlen=200, nheads=4, headdim=64, dsta
                    ngroups=1, chunk=64, io="bf16", seed=100, **kw) -> Workload:
     """Ad-hoc workload with the same value distributions (for tests)."""
     return Workload(name, batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io, seed, **kw)
+
+
+# --------------------------------------------------------------------------
+# Gated DeltaNet decode tokens (the FPGA decode page's second fixed-state
+# recurrence).  The page fixes the shapes (2 MB of fp32 state over 32 value
+# heads: dk = dv = 128; value heads grouped two per query/key head) and no
+# value distributions; the draw below follows what the recurrence expects of
+# its inputs: unit-norm keys and queries, a decay gate g in (0.8, 1) and a write
+# strength beta in (0.1, 0.9), values ~ N(0, 1), the state ~ N(0, 1) / sqrt(dk).
+# --------------------------------------------------------------------------
+GDN_SHAPE = dict(qk_heads=16, v_heads=32, dk=128, dv=128)
+
+
+def gdn_tokens(seed: int, steps: int, batch: int, qk_heads: int, v_heads: int, dk: int, dv: int,
+               io: str = "bf16"):
+    """q, k [T, b, Hk, dk], v [T, b, Hv, dv] (bf16 bits or fp32), g, beta [T, b, Hv] fp32,
+    and state0 [b, Hv, dk, dv] fp32."""
+    rng = _rng(np.random.SeedSequence(seed))
+    q = rng.standard_normal((steps, batch, qk_heads, dk), dtype=np.float32)
+    k = rng.standard_normal((steps, batch, qk_heads, dk), dtype=np.float32)
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    v = rng.standard_normal((steps, batch, v_heads, dv), dtype=np.float32)
+    g = rng.uniform(0.8, 1.0, (steps, batch, v_heads)).astype(np.float32)
+    beta = rng.uniform(0.1, 0.9, (steps, batch, v_heads)).astype(np.float32)
+    state0 = (rng.standard_normal((batch, v_heads, dk, dv), dtype=np.float32)
+              / np.float32(math.sqrt(dk)))
+    return dict(q=_store(q, io), k=_store(k, io), v=_store(v, io), g=g, beta=beta,
+                state0=state0)

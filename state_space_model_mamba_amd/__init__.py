@@ -15,6 +15,7 @@ to pass u instead of dt; the step size is then softplus(u + dt_bias) in the kern
     ssd_decode_steps(x, dt, A, B, C, D, state, y=None) -> y   (S steps in one launch)
     ssd_chunk_scan_timed(...) -> (y, final_state, [(kernel, ms), ...])
     ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, ...) -> (y, final_states)
+    ssd_gdn_decode_step(q, k, v, g, beta, state, o=None) -> o   (Gated DeltaNet step)
 """
 from __future__ import annotations
 
@@ -30,7 +31,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
           4: "SSD_ERR_ALIAS", 5: "SSD_ERR_WORKSPACE", 6: "SSD_ERR_DEVICE", 7: "SSD_ERR_ALIGNMENT"}
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_state_init", "ssd_chunk_scan_workspace_size",
            "ssd_chunk_scan", "ssd_decode_step", "ssd_decode_steps", "ssd_chunk_scan_timed",
-           "ssd_chunk_scan_varlen_workspace_size", "ssd_chunk_scan_varlen")
+           "ssd_chunk_scan_varlen_workspace_size", "ssd_chunk_scan_varlen",
+           "ssd_gdn_decode_step")
 
 
 class SsdError(RuntimeError):
@@ -45,6 +47,12 @@ class SsdDims(ctypes.Structure):
                 ("dstate", ctypes.c_int64), ("ngroups", ctypes.c_int64),
                 ("chunk", ctypes.c_int64), ("io_dtype", ctypes.c_int32),
                 ("flags", ctypes.c_int32), ("dt_bias", ctypes.c_void_p)]
+
+
+class SsdGdnDims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int64), ("qk_heads", ctypes.c_int64),
+                ("v_heads", ctypes.c_int64), ("dk", ctypes.c_int64), ("dv", ctypes.c_int64),
+                ("io_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 _lib = None
@@ -86,6 +94,8 @@ def load(path: str | None = None):
     lib.ssd_chunk_scan_varlen_workspace_size.restype = ctypes.c_int
     lib.ssd_chunk_scan_varlen.argtypes = [dims, cu] + [vp] * 10 + [ctypes.c_size_t, vp]
     lib.ssd_chunk_scan_varlen.restype = ctypes.c_int
+    lib.ssd_gdn_decode_step.argtypes = [ctypes.POINTER(SsdGdnDims)] + [vp] * 8
+    lib.ssd_gdn_decode_step.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -259,3 +269,18 @@ def ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, initial_states=N
         _ptr(initial_states), _ptr(y), _ptr(final_states), _ptr(workspace), ws_bytes,
         _stream(stream)))
     return y, final_states
+
+
+def ssd_gdn_decode_step(q, k, v, g, beta, state, o=None, stream=None):
+    """One Gated DeltaNet decode step: q, k [B, Hk, dk], v [B, Hv, dv], g, beta [B, Hv]
+    fp32, state [B, Hv, dk, dv] fp32 updated in place; returns o [B, Hv, dv]."""
+    import torch
+    bsz, Hk, dk = q.shape
+    Hv, dv = v.shape[1], v.shape[2]
+    d = SsdGdnDims(bsz, Hk, Hv, dk, dv, _io_dtype(q), 0)
+    if o is None:
+        o = torch.empty_like(v)
+    _check("ssd_gdn_decode_step", load().ssd_gdn_decode_step(
+        ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
+        _stream(stream)))
+    return o

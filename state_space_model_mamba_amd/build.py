@@ -18,8 +18,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIBRARY = os.path.join(PKG, "libssd.so")
-SOURCES = ["ssd_api.cpp", "ssd_decode.hip", "ssd_decode_steps.hip", "ssd_scan_f32.hip",
-           "ssd_scan_bf16.hip"]
+SOURCES = ["ssd_api.cpp", "ssd_decode.hip", "ssd_decode_steps.hip", "ssd_gdn.hip",
+           "ssd_scan_f32.hip", "ssd_scan_bf16.hip"]
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -519,3 +519,45 @@ SSD_EXPORT ssd_status ssd_chunk_scan_varlen(const ssd_dims *dims, const int64_t 
         return st;
     return call(true);
 }
+
+SSD_EXPORT ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const void *k,
+                                          const void *v, const float *g, const float *beta,
+                                          float *state, void *o, void *stream)
+{
+    if (!dims)
+        return SSD_ERR_NULL;
+    if (dims->reserved != 0 || dims->batch < 0 || dims->qk_heads < 1 || dims->v_heads < 1 ||
+        dims->v_heads % dims->qk_heads != 0)
+        return SSD_ERR_SHAPE;
+    if (dims->io_dtype != SSD_F32 && dims->io_dtype != SSD_BF16)
+        return SSD_ERR_UNSUPPORTED;
+    const int64_t Bn = dims->batch, Hk = dims->qk_heads, Hv = dims->v_heads, dk = dims->dk,
+                  dv = dims->dv;
+    if ((dk != 64 && dk != 128 && dk != 256) || (dv != 64 && dv != 128 && dv != 256))
+        return SSD_ERR_UNSUPPORTED;
+    int64_t t;
+    if (!mul_ok(Bn, Hv, &t) || !mul_ok(t, dk, &t) || !mul_ok(t, dv, &t) || !mul_ok(t, 4, &t) ||
+        !mul_ok(Bn, Hk, &t))
+        return SSD_ERR_SHAPE;
+    if (Bn * Hv * (dv / 64) > INT32_MAX || Hv > kMaxHeads)
+        return SSD_ERR_UNSUPPORTED;
+    if (Bn == 0)
+        return SSD_OK;
+    if (!q || !k || !v || !g || !beta || !state || !o)
+        return SSD_ERR_NULL;
+    const int64_t esz = dims->io_dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(state, 16) || !aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) ||
+        !aligned(o, esz) || !aligned(g, 4) || !aligned(beta, 4))
+        return SSD_ERR_ALIGNMENT;
+    const Span ss = span(state, Bn * Hv * dk * dv * 4), so = span(o, Bn * Hv * dv * esz);
+    const Span ins[] = {span(q, Bn * Hk * dk * esz), span(k, Bn * Hk * dk * esz),
+                        span(v, Bn * Hv * dv * esz), span(g, Bn * Hv * 4), span(beta, Bn * Hv * 4)};
+    for (const Span &in : ins)
+        if (overlap(so, in) || overlap(ss, in))
+            return SSD_ERR_ALIAS;
+    if (overlap(so, ss))
+        return SSD_ERR_ALIAS;
+    return device_status(ssd::launch_gdn_decode(dims->io_dtype == SSD_BF16, Bn, Hk, Hv, dk, dv, q,
+                                                k, v, g, beta, state, o,
+                                                static_cast<hipStream_t>(stream)));
+}

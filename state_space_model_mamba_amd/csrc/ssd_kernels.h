@@ -59,6 +59,12 @@ hipError_t launch_decode_steps(int bf16, int64_t S, int64_t B, int64_t H, int64_
                                const void *Bm, const void *Cm, const float *D, float *state,
                                void *y, DtPrep prep, hipStream_t s);
 
+// Gated DeltaNet decode step over B x Hv value heads: q, k [B, Hk, dk],
+// v, o [B, Hv, dv], g, beta [B, Hv], state [B, Hv, dk, dv] (updated in place).
+hipError_t launch_gdn_decode(int bf16, int64_t B, int64_t Hk, int64_t Hv, int64_t dk, int64_t dv,
+                             const void *q, const void *k, const void *v, const float *g,
+                             const float *beta, float *state, void *o, hipStream_t s);
+
 // fp32 chunked scan (VALU), P <= 64, N <= 128, Q <= 256.
 hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                            int64_t Q, const float *x, const float *dt, const float *A,

@@ -227,3 +227,34 @@ def test_varlen_host_logic(lib):
     rc = lib.ssd_chunk_scan_varlen(ctypes.byref(d), arr, *[p(FAKE + (k << 33)) for k in range(6)],
                                    None, p(FAKE + (6 << 33)), p(FAKE + (7 << 33)), None, 0, None)
     assert rc == 7
+
+
+def test_gdn_validation(lib):
+    """ssd_gdn_decode_step rejects bad arguments before any launch (CPU only)."""
+    p = ctypes.c_void_p
+
+    def gd(**kw):
+        base = dict(batch=4, qk_heads=16, v_heads=32, dk=128, dv=128, io_dtype=ssd.SSD_BF16,
+                    reserved=0)
+        base.update(kw)
+        return ssd.SsdGdnDims(**base)
+
+    args = [p(FAKE + (k << 33)) for k in range(7)]   # q, k, v, g, beta, state, o
+
+    def call(d, *over):
+        a = list(args)
+        for i, v in over:
+            a[i] = v
+        return lib.ssd_gdn_decode_step(ctypes.byref(d), *a, None)
+
+    assert lib.ssd_gdn_decode_step(None, *args, None) == 1
+    assert call(gd(), (0, None)) == 1
+    assert call(gd(v_heads=24, qk_heads=16)) == 2      # Hv % Hk != 0
+    assert call(gd(reserved=1)) == 2
+    assert call(gd(dk=96)) == 3
+    assert call(gd(dv=512)) == 3
+    assert call(gd(io_dtype=5)) == 3
+    assert call(gd(), (5, p(FAKE + (5 << 33) + 8))) == 7          # misaligned state
+    assert call(gd(), (6, p(FAKE + (5 << 33) + 64))) == 4         # o inside the state
+    assert call(gd(), (5, p(FAKE + (2 << 33) + 64))) == 4         # state inside v
+    assert call(gd(batch=0), *[(i, None) for i in range(7)]) == 0

@@ -1,0 +1,91 @@
+"""GPU parity of ssd_gdn_decode_step (Gated DeltaNet decode, one read and one
+write of the state) against the fp64 three-pass oracle (oracle.gdn).
+
+Several consecutive steps are run and every output and the final state are
+compared, so an error in the state carried from step to step shows too.
+Tolerances as for the SSD paths: 2e-2 relative for bf16 I/O (o rounded to
+bf16), 1e-5 for fp32; the state is fp32 on both sides.
+"""
+import numpy as np
+import pytest
+import torch
+
+import ssd_inputs as si
+import state_space_model_mamba_amd as ssd
+from oracle import gdn
+from parity import TOL, dev, host, rel
+
+pytestmark = pytest.mark.gpu
+
+
+def run(tok, io, steps):
+    q, k, v = dev(tok["q"], io), dev(tok["k"], io), dev(tok["v"], io)
+    g, beta = dev(tok["g"]), dev(tok["beta"])
+    state = dev(tok["state0"].copy())
+    outs = torch.empty_like(v)
+    for t in range(steps):
+        ssd.ssd_gdn_decode_step(q[t], k[t], v[t], g[t], beta[t], state, o=outs[t])
+    torch.cuda.synchronize()
+    return host(outs), host(state)
+
+
+def oracle_run(tok, io):
+    w = lambda a: si.widen(a, io)
+    return gdn.gdn_decode_steps(tok["state0"], w(tok["q"]), w(tok["k"]), w(tok["v"]),
+                                tok["g"].astype(np.float64), tok["beta"].astype(np.float64))
+
+
+def check(o, s, oref, sref, tol, what):
+    assert np.isfinite(o).all() and np.isfinite(s).all(), what
+    assert rel(o, oref) <= tol, f"{what}: o rel {rel(o, oref):.3e}"
+    assert rel(s, sref) <= tol, f"{what}: state rel {rel(s, sref):.3e}"
+    T, B, Hv = o.shape[:3]
+    for b in range(B):
+        for j in range(Hv):
+            eo, es = rel(o[:, b, j], oref[:, b, j]), rel(s[b, j], sref[b, j])
+            assert eo <= tol and es <= tol, f"{what}[b={b}, head {j}]: o {eo:.3e}, state {es:.3e}"
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("batch", [1, 8])
+def test_gdn_page_shape(io, batch):
+    """The page's shape: 32 value heads over 16 query/key heads, 128 x 128 fp32
+    state per value head (2 MB per sequence), 12 steps."""
+    sh = si.GDN_SHAPE
+    tok = si.gdn_tokens(300 + batch, 12, batch, sh["qk_heads"], sh["v_heads"], sh["dk"], sh["dv"], io)
+    o, s = run(tok, io, 12)
+    oref, sref = oracle_run(tok, io)
+    check(o, s, oref, sref, TOL[io], f"gdn {io} b={batch}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv,Hk,Hv", [(64, 64, 2, 2), (64, 256, 1, 4), (256, 64, 3, 6),
+                                         (256, 256, 2, 4), (128, 64, 4, 4)])
+def test_gdn_shapes(io, dk, dv, Hk, Hv):
+    tok = si.gdn_tokens(dk * 7 + dv + Hv, 5, 3, Hk, Hv, dk, dv, io)
+    o, s = run(tok, io, 5)
+    oref, sref = oracle_run(tok, io)
+    check(o, s, oref, sref, TOL[io], f"gdn {io} dk={dk} dv={dv}")
+
+
+def test_gdn_batch_256_sampled():
+    """Batch 256 at the page's shape (537 MB of state), 3 steps; sampled sequences
+    against the oracle and the whole batch finite and deterministic."""
+    sh = si.GDN_SHAPE
+    tok = si.gdn_tokens(311, 3, 256, sh["qk_heads"], sh["v_heads"], sh["dk"], sh["dv"], "bf16")
+    o1, s1 = run(tok, "bf16", 3)
+    o2, s2 = run(tok, "bf16", 3)
+    assert np.array_equal(o1, o2) and np.array_equal(s1, s2)
+    seqs = [0, 77, 255]
+    sub = {k: (v[:, seqs] if k != "state0" else v[seqs]) for k, v in tok.items()}
+    oref, sref = oracle_run(sub, "bf16")
+    check(o1[:, seqs], s1[seqs], oref, sref, TOL["bf16"], "gdn b=256")
+
+
+def test_gdn_empty_batch():
+    z = torch.empty((0, 16, 128), dtype=torch.bfloat16, device="cuda")
+    v = torch.empty((0, 32, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.empty((0, 32), dtype=torch.float32, device="cuda")
+    st = torch.empty((0, 32, 128, 128), dtype=torch.float32, device="cuda")
+    out = ssd.ssd_gdn_decode_step(z, z, v, g, g, st)
+    assert out.shape == v.shape
