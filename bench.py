@@ -500,6 +500,28 @@ def cpu_baseline_decode(w, batch=256, nseq=64, steps=200):
             "sample": f"{nseq} of {batch} sequences x {steps} steps; scaled by {nseq}/{batch}"}
 
 
+def cpu_baseline_gdn(nseq=32, steps=40, batch=256):
+    """The fp64 GDN oracle (three passes, numpy, BLAS held to one thread) on `nseq`
+    sequences of the page's shape for `steps` steps; steps/s scaled to the full batch."""
+    from threadpoolctl import threadpool_limits
+
+    from oracle import gdn
+    import ssd_inputs as si
+
+    sh = si.GDN_SHAPE
+    tok = si.gdn_tokens(401, steps, nseq, sh["qk_heads"], sh["v_heads"], sh["dk"], sh["dv"], "f32")
+    S = tok["state0"].astype(np.float64)
+    with threadpool_limits(1):
+        t0 = time.perf_counter()
+        for t in range(steps):
+            _, S = gdn.gdn_decode_step(S, tok["q"][t], tok["k"][t], tok["v"][t], tok["g"][t],
+                                       tok["beta"][t])
+        T = time.perf_counter() - t0
+    return {"value": steps / (T * batch / nseq), "unit": "steps/s", "cores": 1, "kind": "oracle",
+            "sample": f"{nseq} of {batch} sequences x {steps} steps, one thread; "
+                      f"{T:.1f} s, scaled by {nseq}/{batch}"}
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -611,6 +633,7 @@ def main():
         }
         line["gdn_decode"] = bench_gdn(args)
         if not args.no_cpu_baseline:
+            line["gdn_decode"]["cpu_baseline"] = cpu_baseline_gdn()
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(wd)
             line["decode_steps"]["cpu_baseline"] = dict(
                 line["decode"]["cpu_baseline"],
