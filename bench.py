@@ -438,7 +438,7 @@ def bench_varlen(args):
                         f"lengths {list(VARLEN_LENGTHS)} ({T} tokens), 80 heads x 64, dstate 128, "
                         f"chunk 256, bf16",
             "event_ms_per_call": ms, "tokens_per_s": T / (ms * 1e-3),
-            "scan_calls": runs}
+            "runs_of_equal_length": runs, "kernel_launches": 2 * ((runs + 7) // 8)}
 
 
 def cpu_baseline_prefill(w, npairs=None):

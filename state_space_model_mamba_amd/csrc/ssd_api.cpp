@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <vector>
 
 #include "ssd.h"
 #include "ssd_kernels.h"
@@ -142,7 +143,7 @@ size_t scan_workspace(const ssd_dims *d)
 ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const float *A,
                     const void *B, const void *C, const float *D, const float *init, void *y,
                     float *fin, void *ws, size_t ws_bytes, hipStream_t s, ssd::EventLog *log,
-                    bool launch = true)
+                    bool launch = true, bool check_ws = true)
 {
     ssd_status st = check_dims(d, true);
     if (st != SSD_OK)
@@ -173,7 +174,7 @@ ssd_status run_scan(const ssd_dims *d, const void *x, const float *dt, const flo
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
         !aligned(dt, 4) || !aligned(A, 4) || !aligned(D, 4))
         return SSD_ERR_ALIGNMENT;
-    const size_t need = scan_workspace(d);
+    const size_t need = check_ws ? scan_workspace(d) : 0;
     if (need > 0 && (!ws || ws_bytes < need))
         return SSD_ERR_WORKSPACE;
     if (need > 0 && !aligned(ws, 16))
@@ -240,6 +241,32 @@ ssd_status varlen_check(const ssd_dims *d, const int64_t *cu)
     return scan_supported(d);
 }
 
+// bf16 runs are scanned kMaxRuns at a time, each group in one state-kernel and
+// one scan-kernel launch; a run plans for its share of the 256 CUs
+// (proportional to its tokens) and gets its own workspace region.
+struct RunRef {
+    int64_t seq, tok, B, L;
+};
+
+std::vector<std::vector<RunRef>> bf16_groups(const ssd_dims *d, const int64_t *cu);
+
+size_t group_plans(const ssd_dims *d, const std::vector<RunRef> &grp,
+                   std::vector<ssd::Bf16Plan> *plans)
+{
+    int64_t total = 0;
+    for (const RunRef &r : grp)
+        total += r.B * r.L;
+    size_t bytes = 0;
+    for (const RunRef &r : grp) {
+        const int64_t cus = std::max<int64_t>(8, (256 * r.B * r.L + total - 1) / std::max<int64_t>(total, 1));
+        const ssd::Bf16Plan p = ssd::plan_scan_bf16(r.B, r.L, d->nheads, d->ngroups, d->chunk, cus);
+        if (plans)
+            plans->push_back(p);
+        bytes += (p.ws_bytes + 255) / 256 * 256;
+    }
+    return bytes;
+}
+
 template <class F>
 ssd_status for_each_run(const ssd_dims *d, const int64_t *cu, F f)
 {
@@ -257,6 +284,22 @@ ssd_status for_each_run(const ssd_dims *d, const int64_t *cu, F f)
         i = j;
     }
     return SSD_OK;
+}
+
+std::vector<std::vector<RunRef>> bf16_groups(const ssd_dims *d, const int64_t *cu)
+{
+    std::vector<std::vector<RunRef>> groups(1);
+    for_each_run(d, cu, [&](const ssd_dims &r, int64_t seq, int64_t tok) {
+        if (r.seqlen == 0)
+            return SSD_OK;
+        if ((int)groups.back().size() == ssd::kMaxRuns)
+            groups.emplace_back();
+        groups.back().push_back(RunRef{seq, tok, r.batch, r.seqlen});
+        return SSD_OK;
+    });
+    if (groups.back().empty())
+        groups.pop_back();
+    return groups;
 }
 
 }  // namespace
@@ -461,10 +504,10 @@ SSD_EXPORT ssd_status ssd_chunk_scan_varlen_workspace_size(const ssd_dims *dims,
     if (!bytes)
         return SSD_ERR_NULL;
     size_t need = 0;
-    for_each_run(dims, cu_seqlens, [&](const ssd_dims &r, int64_t, int64_t) {
-        need = std::max(need, scan_workspace(&r));
-        return SSD_OK;
-    });
+    if (dims->io_dtype == SSD_BF16) {
+        for (const auto &grp : bf16_groups(dims, cu_seqlens))
+            need = std::max(need, group_plans(dims, grp, nullptr));
+    }
     *bytes = need;
     return SSD_OK;
 }
@@ -501,23 +544,59 @@ SSD_EXPORT ssd_status ssd_chunk_scan_varlen(const ssd_dims *dims, const int64_t 
     if (initial_states && initial_states != final_states && overlap(sfin, sinit))
         return SSD_ERR_ALIAS;
     const hipStream_t s = static_cast<hipStream_t>(stream);
+    const bool bf16 = dims->io_dtype == SSD_BF16;
+    const char *xb = static_cast<const char *>(x), *bb = static_cast<const char *>(B),
+               *cb = static_cast<const char *>(C);
+    char *yb = static_cast<char *>(y);
+    // fp32 runs: one scan call each (launch = true); bf16 runs: validation only
+    // here (their workspace is the group's, checked below), and empty runs
+    // (the state handed through) are enqueued by the same call
     auto call = [&](bool launch) {
         return for_each_run(dims, cu_seqlens, [&](const ssd_dims &r, int64_t seq, int64_t tok) {
-            const char *xb = static_cast<const char *>(x), *bb = static_cast<const char *>(B),
-                       *cb = static_cast<const char *>(C);
-            char *yb = static_cast<char *>(y);
+            const bool go = launch && (!bf16 || r.seqlen == 0);
             return run_scan(&r, xb ? xb + tok * H * P * esz : nullptr, dt ? dt + tok * H : nullptr,
                             A, bb ? bb + tok * G * N * esz : nullptr,
                             cb ? cb + tok * G * N * esz : nullptr, D,
                             initial_states ? initial_states + seq * HPN : nullptr,
                             yb ? yb + tok * H * P * esz : nullptr, final_states + seq * HPN,
-                            workspace, workspace_bytes, s, nullptr, launch);
+                            workspace, workspace_bytes, s, nullptr, go, !bf16);
         });
     };
     // every run is validated before the first is enqueued
     if ((st = call(false)) != SSD_OK)
         return st;
-    return call(true);
+    std::vector<std::vector<RunRef>> groups;
+    if (bf16) {
+        groups = bf16_groups(dims, cu_seqlens);
+        size_t need = 0;
+        for (const auto &grp : groups)
+            need = std::max(need, group_plans(dims, grp, nullptr));
+        if (need > 0 && (!workspace || workspace_bytes < need))
+            return SSD_ERR_WORKSPACE;
+        if (need > 0 && !aligned(workspace, 16))
+            return SSD_ERR_ALIGNMENT;
+    }
+    if ((st = call(true)) != SSD_OK)
+        return st;
+    for (const auto &grp : groups) {
+        std::vector<ssd::Bf16Plan> plans;
+        group_plans(dims, grp, &plans);
+        ssd::Bf16Run runs[ssd::kMaxRuns];
+        char *wsp = static_cast<char *>(workspace);
+        for (size_t r = 0; r < grp.size(); ++r) {
+            const RunRef &u = grp[r];
+            runs[r] = ssd::Bf16Run{plans[r], u.B, u.L, xb + u.tok * H * P * esz, dt + u.tok * H,
+                                   bb + u.tok * G * N * esz, cb + u.tok * G * N * esz,
+                                   initial_states ? initial_states + u.seq * HPN : nullptr,
+                                   yb + u.tok * H * P * esz, final_states + u.seq * HPN, wsp};
+            wsp += (plans[r].ws_bytes + 255) / 256 * 256;
+        }
+        const hipError_t e = ssd::launch_scan_bf16_multi(runs, (int)grp.size(), H, G, dims->chunk,
+                                                         A, D, dt_prep(dims), s);
+        if (e != hipSuccess)
+            return SSD_ERR_DEVICE;
+    }
+    return SSD_OK;
 }
 
 SSD_EXPORT ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const void *k,

@@ -85,12 +85,30 @@ struct Bf16Plan {
     size_t decay_bytes;    // B*H*nslot*4
     size_t ws_bytes;       // total workspace
 };
-Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q);
+// cus: the CUs the problem may count on (fewer when it shares a launch).
+Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, int64_t cus = 256);
 
 hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
                             int64_t Q, const void *x, const float *dt, const float *A,
                             const void *Bm, const void *Cm, const float *D, const float *init,
                             void *y, float *fin, void *ws, DtPrep prep, hipStream_t s,
                             EventLog *log);
+
+// Up to kMaxRuns independent bf16 scans (batch B, length L > 0 each; same H, G,
+// Q, A, D, step-size prep) in one state-kernel and one scan-kernel launch.
+constexpr int kMaxRuns = 8;
+struct Bf16Run {
+    Bf16Plan plan;
+    int64_t B, L;
+    const void *x;
+    const float *dt;
+    const void *Bm, *Cm;
+    const float *init;
+    void *y;
+    float *fin;
+    void *ws;   // plan.ws_bytes of workspace for this run
+};
+hipError_t launch_scan_bf16_multi(const Bf16Run *runs, int nruns, int64_t H, int64_t G, int64_t Q,
+                                  const float *A, const float *D, DtPrep prep, hipStream_t s);
 
 }  // namespace ssd

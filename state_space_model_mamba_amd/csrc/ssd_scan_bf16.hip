@@ -521,14 +521,17 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &p
 
 // The scan kernel: y of segment `seg` from the state entering it and, for the
 // last segment, the final state.
+// `bid` of `nblk` is the work-group's index among those of its launch (or of
+// its run, when one launch covers several problems).
 template <int kH, bool kSp>
-__device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm)
+__device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, int64_t bid,
+                                          int64_t nblk)
 {
     constexpr int kHeads = kH, kWaves = 2 * kH;
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     const int hs = w >> 1;                                // head slot in the work-group
     const int ph = w & 1;                                 // P half: p = 32 ph .. 32 ph + 31
-    const int64_t j = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t j = xcd_remap(bid, nblk);
     const int nquad = a.G * a.nq;
     const int quad = (int)(j % nquad);
     const int64_t r = j / nquad;
@@ -893,7 +896,7 @@ template <int n> __device__ __forceinline__ void wait_vmcnt()
 }
 
 template <bool kSp>
-__global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
+__device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, int64_t nblk)
 {
     __shared__ __align__(16) unsigned char sB0[kT * kBRow], sB1[kT * kBRow], sB2[kT * kBRow];
     __shared__ __align__(16) unsigned char sX0[kStHeads][kT * kXRow], sX1[kStHeads][kT * kXRow],
@@ -903,7 +906,7 @@ __global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
 
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     const int hs = w >> 1, ph = w & 1;
-    const int64_t j = xcd_remap(blockIdx.x, gridDim.x);
+    const int64_t j = xcd_remap(bid, nblk);
     const int nquad = a.G * a.nq;
     const int quad = (int)(j % nquad);
     const int64_t r = j / nquad;
@@ -1039,13 +1042,61 @@ __global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
             *reinterpret_cast<f32x4 *>(dst + zoff + 16 * q * kN + 16 * nb) = Z[nb][q] * sc;
 }
 
+// State kernel: the end state of every unit of segments 0 .. nseg-2, and its decay.
+template <bool kSp>
+__global__ __launch_bounds__(kStThreads, 1) void seg_state_kernel(SegArgs a)
+{
+    seg_state_body<kSp>(a, blockIdx.x, gridDim.x);
+}
+
 // Scan kernel: y of every segment from its entering state, and the final state.
 // kSp: the dt input holds u and the step size is softplus(u + dt_bias[h]).
 template <bool kSp>
 __global__ __launch_bounds__(Geom<kScanHeads>::kThreads, 1) void chunk_scan_kernel(SegArgs a)
 {
     __shared__ ScanSmem<kScanHeads> sm;
-    scan_body<kScanHeads, kSp>(a, sm);
+    scan_body<kScanHeads, kSp>(a, sm, blockIdx.x, gridDim.x);
+}
+
+// Several independent problems (the runs of equal length of a packed batch)
+// in one launch: run r owns work-groups wg0[r] .. wg0[r] + nwg[r] - 1, its
+// start a multiple of 8 so that the work-group -> XCD mapping inside a run is
+// the same as in a launch of its own; the padding work-groups return.
+struct MultiArgs {
+    SegArgs run[kMaxRuns];
+    int wg0[kMaxRuns + 1];
+    int nwg[kMaxRuns];
+    int nruns;
+};
+
+__device__ __forceinline__ int multi_run(const MultiArgs &m, int bid)
+{
+    int r = 0;
+#pragma unroll
+    for (int k = 1; k < kMaxRuns; ++k)
+        r += (k < m.nruns && bid >= m.wg0[k]) ? 1 : 0;
+    return r;
+}
+
+template <bool kSp>
+__global__ __launch_bounds__(kStThreads, 1) void seg_state_multi_kernel(MultiArgs m)
+{
+    const int r = multi_run(m, blockIdx.x);
+    const int local = (int)blockIdx.x - m.wg0[r];
+    if (local >= m.nwg[r])
+        return;
+    seg_state_body<kSp>(m.run[r], local, m.nwg[r]);
+}
+
+template <bool kSp>
+__global__ __launch_bounds__(Geom<kScanHeads>::kThreads, 1) void chunk_scan_multi_kernel(MultiArgs m)
+{
+    __shared__ ScanSmem<kScanHeads> sm;
+    const int r = multi_run(m, blockIdx.x);
+    const int local = (int)blockIdx.x - m.wg0[r];
+    if (local >= m.nwg[r])
+        return;
+    scan_body<kScanHeads, kSp>(m.run[r], sm, local, m.nwg[r]);
 }
 
 int64_t env_int(const char *name, int64_t dflt)
@@ -1066,8 +1117,9 @@ static size_t align256(size_t n)
     return (n + 255) / 256 * 256;
 }
 
-Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
+Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, int64_t cus)
 {
+    const int64_t kCUs = std::max<int64_t>(1, cus);
     Bf16Plan p{};
     p.nchunks = (L + Q - 1) / Q;
     const int64_t hg = G > 0 ? H / G : 1;
@@ -1132,14 +1184,14 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q)
     return p;
 }
 
-hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
-                            int64_t Q, const void *x, const float *dt, const float *A,
-                            const void *Bm, const void *Cm, const float *D, const float *init,
-                            void *y, float *fin, void *ws, DtPrep prep, hipStream_t s,
-                            EventLog *log)
+namespace {
+
+// The kernel arguments of one problem; nq and nseg_launch are set per kernel.
+SegArgs seg_args(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q,
+                 const void *x, const float *dt, const float *A, const void *Bm, const void *Cm,
+                 const float *D, const float *init, void *y, float *fin, void *ws, DtPrep prep)
 {
-    if (B * H == 0 || L == 0)
-        return hipSuccess;
+    (void)B;
     SegArgs a{};
     a.x = static_cast<const __bf16 *>(x);
     a.dt = dt;
@@ -1155,8 +1207,6 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     a.H = (int)H;
     a.G = (int)G;
     a.hg = (int)(H / G);
-    const int nq3 = (a.hg + kScanHeads - 1) / kScanHeads;
-    const int nq1 = (a.hg + kStHeads - 1) / kStHeads;
     a.seg_tokens = plan.chunks_per_seg * Q;
     a.unit_tokens = plan.unit_tokens;
     a.nseg = (int)plan.nseg;
@@ -1167,6 +1217,32 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     char *wsb = static_cast<char *>(ws);
     a.ws_state = reinterpret_cast<float *>(wsb);
     a.ws_decay = reinterpret_cast<float *>(wsb + align256(plan.state_bytes));
+    return a;
+}
+
+int state_quads(const SegArgs &a)
+{
+    return (a.hg + kStHeads - 1) / kStHeads;
+}
+
+int scan_quads(const SegArgs &a)
+{
+    return (a.hg + kScanHeads - 1) / kScanHeads;
+}
+
+}  // namespace
+
+hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
+                            int64_t Q, const void *x, const float *dt, const float *A,
+                            const void *Bm, const void *Cm, const float *D, const float *init,
+                            void *y, float *fin, void *ws, DtPrep prep, hipStream_t s,
+                            EventLog *log)
+{
+    if (B * H == 0 || L == 0)
+        return hipSuccess;
+    SegArgs a = seg_args(plan, B, L, H, G, Q, x, dt, A, Bm, Cm, D, init, y, fin, ws, prep);
+    const int nq3 = scan_quads(a);
+    const int nq1 = state_quads(a);
     hipError_t e = log_begin(log, s);
     if (e != hipSuccess)
         return e;
@@ -1191,6 +1267,59 @@ hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t 
     if ((e = hipGetLastError()) != hipSuccess)
         return e;
     return log_kernel(log, "chunk_scan_kernel", s);
+}
+
+hipError_t launch_scan_bf16_multi(const Bf16Run *runs, int nruns, int64_t H, int64_t G, int64_t Q,
+                                  const float *A, const float *D, DtPrep prep, hipStream_t s)
+{
+    if (nruns < 1 || nruns > kMaxRuns)
+        return hipErrorInvalidValue;
+    MultiArgs m1{}, m3{};   // state kernel, scan kernel
+    int wg1 = 0, wg3 = 0;
+    for (int r = 0; r < nruns; ++r) {
+        const Bf16Run &u = runs[r];
+        SegArgs a = seg_args(u.plan, u.B, u.L, H, G, Q, u.x, u.dt, A, u.Bm, u.Cm, D, u.init, u.y,
+                             u.fin, u.ws, prep);
+        SegArgs a1 = a, a3 = a;
+        a1.nq = state_quads(a);
+        a1.nseg_launch = (a.nseg - 1) * a.nsub;
+        a3.nq = scan_quads(a);
+        a3.nseg_launch = a.nseg;
+        const int64_t n1 = u.plan.nseg > 1 ? u.B * G * a1.nq * a1.nseg_launch : 0;
+        const int64_t n3 = u.B * G * a3.nq * a3.nseg_launch;
+        if (wg1 + n1 + 8 > INT32_MAX / 2 || wg3 + n3 + 8 > INT32_MAX / 2)
+            return hipErrorInvalidValue;
+        m1.run[r] = a1;
+        m1.wg0[r] = wg1;
+        m1.nwg[r] = (int)n1;
+        wg1 += (int)((n1 + 7) / 8 * 8);
+        m3.run[r] = a3;
+        m3.wg0[r] = wg3;
+        m3.nwg[r] = (int)n3;
+        wg3 += (int)((n3 + 7) / 8 * 8);
+    }
+    m1.nruns = m3.nruns = nruns;
+    for (int r = nruns; r <= kMaxRuns; ++r) {
+        if (r < kMaxRuns) {
+            m1.nwg[r] = m3.nwg[r] = 0;
+        }
+        m1.wg0[r] = wg1;
+        m3.wg0[r] = wg3;
+    }
+    hipError_t e;
+    if (wg1 > 0) {
+        if (prep.softplus)
+            seg_state_multi_kernel<true><<<(unsigned)wg1, kStThreads, 0, s>>>(m1);
+        else
+            seg_state_multi_kernel<false><<<(unsigned)wg1, kStThreads, 0, s>>>(m1);
+        if ((e = hipGetLastError()) != hipSuccess)
+            return e;
+    }
+    if (prep.softplus)
+        chunk_scan_multi_kernel<true><<<(unsigned)wg3, Geom<kScanHeads>::kThreads, 0, s>>>(m3);
+    else
+        chunk_scan_multi_kernel<false><<<(unsigned)wg3, Geom<kScanHeads>::kThreads, 0, s>>>(m3);
+    return hipGetLastError();
 }
 
 }  // namespace ssd

@@ -205,9 +205,12 @@ def test_varlen_host_logic(lib):
         return ws_size(lib, dims(batch=b, seqlen=L, nheads=H, headdim=P, dstate=N, ngroups=G,
                                  chunk=Q))[1]
 
+    # runs of equal length share one launch pair, each planning for its share of
+    # the CUs with a workspace region of its own: at most the runs' own sizes summed
     rc, n = size([0, 8192, 8192 + 100, 8192 + 200, 8192 + 4296])
-    assert rc == 0 and n == max(run_ws(1, 8192), run_ws(2, 100), run_ws(1, 4096))
-    assert size([0, 4096, 8192, 12288, 16384]) == (0, run_ws(4, 4096))   # one run
+    assert rc == 0 and 0 < n <= run_ws(1, 8192) + run_ws(2, 100) + run_ws(1, 4096) + 3 * 256
+    assert n % 256 == 0
+    assert size([0, 4096, 8192, 12288, 16384]) == (0, run_ws(4, 4096))   # one run: the batched scan
     assert size([0, 0, 0])[0] == 0
     assert size([1, 5])[0] == 2                # cu[0] != 0
     assert size([0, 7, 5, 9])[0] == 2          # decreasing
