@@ -327,6 +327,12 @@ def gdn_bytes(b, sh, esz=2) -> int:
             + 2 * b * sh["v_heads"] * 4)
 
 
+def gdn_flops(b, sh) -> int:
+    """Arithmetic of one GDN step per state element: the retrieval and readout
+    products and sums (4 FLOP) and the update g S + k dv (3 FLOP)."""
+    return 7 * b * sh["v_heads"] * sh["dk"] * sh["dv"]
+
+
 def bench_gdn(args):
     """Gated DeltaNet decode (ssd_gdn_decode_step) at the FPGA page's shape: 32 value
     heads over 16 query/key heads, 128 x 128 fp32 state per value head, bf16 q/k/v/o;
@@ -374,8 +380,19 @@ def bench_gdn(args):
         torch.cuda.synchronize()
         gms = e0.elapsed_time(e1) / steps
         nb = gdn_bytes(b, sh)
+        # the same steps as one ssd_gdn_decode_steps launch (state kept on-chip)
+        ssd.ssd_gdn_decode_steps(q, k, v, g, beta, state, o=o)
+        torch.cuda.synchronize()
+        e0.record()
+        ssd.ssd_gdn_decode_steps(q, k, v, g, beta, state, o=o)
+        e1.record()
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / steps
+        fl = gdn_flops(b, sh)
         out[b] = {"event_ms_per_step": ms, "graph_ms_per_step": gms, "bytes_per_step": nb,
-                  "gbs": nb / (ms * 1e-3) / 1e9, "graph_gbs": nb / (gms * 1e-3) / 1e9}
+                  "gbs": nb / (ms * 1e-3) / 1e9, "graph_gbs": nb / (gms * 1e-3) / 1e9,
+                  "steps_launch_ms_per_step": sms,
+                  "steps_launch_tflops": fl / (sms * 1e-3) / 1e12}
         del q, k, v, g, beta, state, o, graph
         torch.cuda.empty_cache()
     r = out[256]
@@ -389,6 +406,14 @@ def bench_gdn(args):
                          "bytes_per_launch": r["bytes_per_step"],
                          "avg_launch_ms": r["event_ms_per_step"]},
             "batches": {str(b): v for b, v in sorted(out.items())},
+            "steps_launch": {"roofline": {
+                "bound": "alu", "kernel": "gdn_steps_kernel", "batch": 256,
+                "achieved": r["steps_launch_tflops"], "peak": FP32_VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": r["steps_launch_tflops"] / FP32_VALU_PEAK_TFLOPS,
+                "flops_per_step": gdn_flops(256, sh),
+                "avg_launch_ms": r["steps_launch_ms_per_step"] * 200},
+                "note": "the same 200 steps as one ssd_gdn_decode_steps launch, the state read and "
+                        "written once and held in registers across the steps"},
             "note": "batch 1 moves 2 MB per step (MALL-resident, launch-bound eager)"}
 
 

@@ -241,6 +241,21 @@ ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const vo
                                void *o, void *stream);
 
 /*
+ * ssd_gdn_decode_steps -- nsteps Gated DeltaNet decode steps in one launch:
+ * the same result as nsteps ssd_gdn_decode_step calls on consecutive slices,
+ * with the state read once, kept on-chip (in registers) across the steps and
+ * written once (section 2A of the FPGA page: a state persistent on-chip is not
+ * re-read from external memory between steps).
+ *   q, k [S, B, Hk, dk]; v, o [S, B, Hv, dv]; g, beta [S, B, Hv]; S = nsteps
+ *   state [B, Hv, dk, dv] fp32, updated in place
+ * nsteps == 0 or B == 0 does nothing; nsteps < 0 is SSD_ERR_SHAPE.  Shapes,
+ * dtypes, alignment and aliasing rules as for ssd_gdn_decode_step.
+ */
+ssd_status ssd_gdn_decode_steps(const ssd_gdn_dims *dims, int64_t nsteps, const void *q,
+                                const void *k, const void *v, const float *g, const float *beta,
+                                float *state, void *o, void *stream);
+
+/*
  * ssd_chunk_scan_timed -- measurement entry point: the same computation as
  * ssd_chunk_scan (same arguments and results), run synchronously; the device
  * time of each kernel the scan launched is written to kernel_ms[0 ..

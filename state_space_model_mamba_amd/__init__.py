@@ -16,6 +16,7 @@ to pass u instead of dt; the step size is then softplus(u + dt_bias) in the kern
     ssd_chunk_scan_timed(...) -> (y, final_state, [(kernel, ms), ...])
     ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, ...) -> (y, final_states)
     ssd_gdn_decode_step(q, k, v, g, beta, state, o=None) -> o   (Gated DeltaNet step)
+    ssd_gdn_decode_steps(q, k, v, g, beta, state, o=None) -> o  (S steps in one launch)
 """
 from __future__ import annotations
 
@@ -32,7 +33,7 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_state_init", "ssd_chunk_scan_workspace_size",
            "ssd_chunk_scan", "ssd_decode_step", "ssd_decode_steps", "ssd_chunk_scan_timed",
            "ssd_chunk_scan_varlen_workspace_size", "ssd_chunk_scan_varlen",
-           "ssd_gdn_decode_step")
+           "ssd_gdn_decode_step", "ssd_gdn_decode_steps")
 
 
 class SsdError(RuntimeError):
@@ -96,6 +97,8 @@ def load(path: str | None = None):
     lib.ssd_chunk_scan_varlen.restype = ctypes.c_int
     lib.ssd_gdn_decode_step.argtypes = [ctypes.POINTER(SsdGdnDims)] + [vp] * 8
     lib.ssd_gdn_decode_step.restype = ctypes.c_int
+    lib.ssd_gdn_decode_steps.argtypes = [ctypes.POINTER(SsdGdnDims), ctypes.c_int64] + [vp] * 8
+    lib.ssd_gdn_decode_steps.restype = ctypes.c_int
     if path is None:
         _lib = lib
     return lib
@@ -283,4 +286,19 @@ def ssd_gdn_decode_step(q, k, v, g, beta, state, o=None, stream=None):
     _check("ssd_gdn_decode_step", load().ssd_gdn_decode_step(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
         _stream(stream)))
+    return o
+
+
+def ssd_gdn_decode_steps(q, k, v, g, beta, state, o=None, stream=None):
+    """S Gated DeltaNet steps in one launch: q, k [S, B, Hk, dk], v [S, B, Hv, dv],
+    g, beta [S, B, Hv]; state [B, Hv, dk, dv] read and written once; returns o [S, B, Hv, dv]."""
+    import torch
+    nsteps, bsz, Hk, dk = q.shape
+    Hv, dv = v.shape[2], v.shape[3]
+    d = SsdGdnDims(bsz, Hk, Hv, dk, dv, _io_dtype(q), 0)
+    if o is None:
+        o = torch.empty_like(v)
+    _check("ssd_gdn_decode_steps", load().ssd_gdn_decode_steps(
+        ctypes.byref(d), ctypes.c_int64(nsteps), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state), _ptr(o), _stream(stream)))
     return o

@@ -599,14 +599,16 @@ SSD_EXPORT ssd_status ssd_chunk_scan_varlen(const ssd_dims *dims, const int64_t 
     return SSD_OK;
 }
 
-SSD_EXPORT ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const void *k,
-                                          const void *v, const float *g, const float *beta,
-                                          float *state, void *o, void *stream)
+namespace {
+
+// Validation shared by the GDN entry points; S = 1 for the single step.
+ssd_status gdn_check(const ssd_gdn_dims *dims, int64_t S, const void *q, const void *k,
+                     const void *v, const float *g, const float *beta, float *state, void *o)
 {
     if (!dims)
         return SSD_ERR_NULL;
     if (dims->reserved != 0 || dims->batch < 0 || dims->qk_heads < 1 || dims->v_heads < 1 ||
-        dims->v_heads % dims->qk_heads != 0)
+        dims->v_heads % dims->qk_heads != 0 || S < 0)
         return SSD_ERR_SHAPE;
     if (dims->io_dtype != SSD_F32 && dims->io_dtype != SSD_BF16)
         return SSD_ERR_UNSUPPORTED;
@@ -615,12 +617,14 @@ SSD_EXPORT ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *
     if ((dk != 64 && dk != 128 && dk != 256) || (dv != 64 && dv != 128 && dv != 256))
         return SSD_ERR_UNSUPPORTED;
     int64_t t;
+    const int64_t Sx = S > 0 ? S : 1;
     if (!mul_ok(Bn, Hv, &t) || !mul_ok(t, dk, &t) || !mul_ok(t, dv, &t) || !mul_ok(t, 4, &t) ||
-        !mul_ok(Bn, Hk, &t))
+        !mul_ok(Sx, Bn, &t) || !mul_ok(t, Hv, &t) || !mul_ok(t, dv, &t) || !mul_ok(t, 4, &t) ||
+        !mul_ok(Sx, Bn, &t) || !mul_ok(t, Hk, &t) || !mul_ok(t, dk, &t) || !mul_ok(t, 4, &t))
         return SSD_ERR_SHAPE;
-    if (Bn * Hv * (dv / 64) > INT32_MAX || Hv > kMaxHeads)
+    if (Bn * Hv * (dv / 64) > INT32_MAX || Hv > kMaxHeads || S > INT32_MAX)
         return SSD_ERR_UNSUPPORTED;
-    if (Bn == 0)
+    if (Bn == 0 || S == 0)
         return SSD_OK;
     if (!q || !k || !v || !g || !beta || !state || !o)
         return SSD_ERR_NULL;
@@ -628,15 +632,41 @@ SSD_EXPORT ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *
     if (!aligned(state, 16) || !aligned(q, esz) || !aligned(k, esz) || !aligned(v, esz) ||
         !aligned(o, esz) || !aligned(g, 4) || !aligned(beta, 4))
         return SSD_ERR_ALIGNMENT;
-    const Span ss = span(state, Bn * Hv * dk * dv * 4), so = span(o, Bn * Hv * dv * esz);
-    const Span ins[] = {span(q, Bn * Hk * dk * esz), span(k, Bn * Hk * dk * esz),
-                        span(v, Bn * Hv * dv * esz), span(g, Bn * Hv * 4), span(beta, Bn * Hv * 4)};
+    const Span ss = span(state, Bn * Hv * dk * dv * 4), so = span(o, S * Bn * Hv * dv * esz);
+    const Span ins[] = {span(q, S * Bn * Hk * dk * esz), span(k, S * Bn * Hk * dk * esz),
+                        span(v, S * Bn * Hv * dv * esz), span(g, S * Bn * Hv * 4),
+                        span(beta, S * Bn * Hv * 4)};
     for (const Span &in : ins)
         if (overlap(so, in) || overlap(ss, in))
             return SSD_ERR_ALIAS;
     if (overlap(so, ss))
         return SSD_ERR_ALIAS;
-    return device_status(ssd::launch_gdn_decode(dims->io_dtype == SSD_BF16, Bn, Hk, Hv, dk, dv, q,
-                                                k, v, g, beta, state, o,
+    return SSD_OK;
+}
+
+}  // namespace
+
+SSD_EXPORT ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const void *k,
+                                          const void *v, const float *g, const float *beta,
+                                          float *state, void *o, void *stream)
+{
+    const ssd_status st = gdn_check(dims, 1, q, k, v, g, beta, state, o);
+    if (st != SSD_OK || dims->batch == 0)
+        return st;
+    return device_status(ssd::launch_gdn_decode(dims->io_dtype == SSD_BF16, dims->batch,
+                                                dims->qk_heads, dims->v_heads, dims->dk, dims->dv,
+                                                q, k, v, g, beta, state, o,
                                                 static_cast<hipStream_t>(stream)));
+}
+
+SSD_EXPORT ssd_status ssd_gdn_decode_steps(const ssd_gdn_dims *dims, int64_t nsteps, const void *q,
+                                           const void *k, const void *v, const float *g,
+                                           const float *beta, float *state, void *o, void *stream)
+{
+    const ssd_status st = gdn_check(dims, nsteps, q, k, v, g, beta, state, o);
+    if (st != SSD_OK || dims->batch == 0 || nsteps == 0)
+        return st;
+    return device_status(ssd::launch_gdn_decode_steps(
+        dims->io_dtype == SSD_BF16, nsteps, dims->batch, dims->qk_heads, dims->v_heads, dims->dk,
+        dims->dv, q, k, v, g, beta, state, o, static_cast<hipStream_t>(stream)));
 }

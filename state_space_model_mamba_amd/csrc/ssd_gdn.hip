@@ -162,6 +162,176 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
     }
 }
 
+// S consecutive steps in one launch (tokens of every step given): the
+// work-group keeps its tile of S in registers across all of them, so the state
+// is read once and written once per launch -- the GPU form of the page's
+// on-chip persistent state (section 2A), which turns decode from memory-bound
+// into compute-bound.  Per step the same two phases as above; q and k go
+// through LDS buffers alternating by step parity, and the next step's q, k, v,
+// g, beta are loaded into registers while the current step computes.
+// q, k [S, B, Hk, DK], v, o [S, B, Hv, dv], g, beta [S, B, Hv].
+template <typename T, int DK, int CT>
+__global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
+    int nsteps, int Bn, int Hk, int Hv, int dv, const T *__restrict__ q,
+    const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
+    const float *__restrict__ beta, float *__restrict__ state, T *__restrict__ o)
+{
+    constexpr int LPR = CT / 4, RPI = 64 / LPR, ROWS = DK / (4 * RPI);
+    static_assert(ROWS >= 1 && ROWS * 4 * RPI == DK, "DK rows split over 4 waves x RPI");
+    constexpr int QK = DK / kGdnThreads > 0 ? DK / kGdnThreads : 1;   // q/k elements per thread
+    __shared__ float sk[2][DK], sq[2][DK];
+    __shared__ float4 part[4 * RPI][LPR][2];
+    __shared__ float4 sdv[LPR];
+    __shared__ float sqk;
+
+    const int tiles = dv / CT;
+    const int bj = blockIdx.x / tiles, tile = blockIdx.x - bj * tiles;
+    const int b = bj / Hv, j = bj - b * Hv, i = j / (Hv / Hk);
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+    const int lg = lane / LPR, lc = lane % LPR;
+    const int c0 = tile * CT + 4 * lc;
+    const int r0 = (w * RPI + lg) * ROWS;
+    const int64_t qks = (int64_t)Bn * Hk * DK, vs = (int64_t)Bn * Hv * dv, gs = (int64_t)Bn * Hv;
+    const T *qb = q + ((int64_t)b * Hk + i) * DK, *kb = k + ((int64_t)b * Hk + i) * DK;
+    const T *vb = v + (int64_t)bj * dv + c0;
+    T *ob = o + (int64_t)bj * dv + c0;
+
+    float *S = state + ((int64_t)bj * DK + r0) * dv + c0;
+    float4 s[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+        s[r] = *reinterpret_cast<const float4 *>(S + (int64_t)r * dv);
+
+    // step t's inputs as this thread needs them (q/k: its share for the LDS
+    // copy; v, g, beta: only the first LPR threads form the delta)
+    struct In {
+        float qv[QK], kv[QK], vv[4], gg, bb;
+    };
+    auto fetch = [&](In &in, int t) {
+        const int64_t tt = t < nsteps ? t : nsteps - 1;
+#pragma unroll
+        for (int e = 0; e < QK; ++e) {
+            const int idx = tid + e * kGdnThreads;
+            in.qv[e] = idx < DK ? gdn_f<T>(qb[tt * qks + idx]) : 0.f;
+            in.kv[e] = idx < DK ? gdn_f<T>(kb[tt * qks + idx]) : 0.f;
+        }
+        if (tid < LPR) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                in.vv[e] = gdn_f<T>(vb[tt * vs + e]);
+        }
+        in.gg = g[tt * gs + bj];
+        in.bb = beta[tt * gs + bj];
+    };
+
+    In cur, nxt;
+    fetch(cur, 0);
+    for (int t = 0; t < nsteps; ++t) {
+        const int pb = t & 1;
+#pragma unroll
+        for (int e = 0; e < QK; ++e) {
+            const int idx = tid + e * kGdnThreads;
+            if (idx < DK) {
+                sq[pb][idx] = cur.qv[e];
+                sk[pb][idx] = cur.kv[e];
+            }
+        }
+        fetch(nxt, t + 1);
+        __syncthreads();   // q, k of step t in LDS; last step's delta consumed
+        float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), pp = pr;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const float kr = sk[pb][r0 + r], qr = sq[pb][r0 + r];
+            pr.x += kr * s[r].x; pr.y += kr * s[r].y; pr.z += kr * s[r].z; pr.w += kr * s[r].w;
+            pp.x += qr * s[r].x; pp.y += qr * s[r].y; pp.z += qr * s[r].z; pp.w += qr * s[r].w;
+        }
+        part[w * RPI + lg][lc][0] = pr;
+        part[w * RPI + lg][lc][1] = pp;
+        if (w == 1) {   // q . k (wave 1, so wave 0 is free for the delta below)
+            float d = 0.f;
+#pragma unroll
+            for (int e = lane; e < DK; e += 64)
+                d += sq[pb][e] * sk[pb][e];
+#pragma unroll
+            for (int off = 32; off > 0; off >>= 1)
+                d += __shfl_xor(d, off, 64);
+            if (lane == 0)
+                sqk = d;
+        }
+        __syncthreads();   // partials and q . k in LDS
+        if (tid < LPR) {
+            float4 R = part[0][tid][0], Pq = part[0][tid][1];
+#pragma unroll
+            for (int m = 1; m < 4 * RPI; ++m) {
+                const float4 a = part[m][tid][0], c = part[m][tid][1];
+                R.x += a.x; R.y += a.y; R.z += a.z; R.w += a.w;
+                Pq.x += c.x; Pq.y += c.y; Pq.z += c.z; Pq.w += c.w;
+            }
+            float4 d;
+            d.x = cur.bb * (cur.vv[0] - cur.gg * R.x);
+            d.y = cur.bb * (cur.vv[1] - cur.gg * R.y);
+            d.z = cur.bb * (cur.vv[2] - cur.gg * R.z);
+            d.w = cur.bb * (cur.vv[3] - cur.gg * R.w);
+            sdv[tid] = d;
+            T *oj = ob + (int64_t)t * vs;
+            const float qk = sqk;
+            oj[0] = gdn_t<T>(cur.gg * Pq.x + qk * d.x);
+            oj[1] = gdn_t<T>(cur.gg * Pq.y + qk * d.y);
+            oj[2] = gdn_t<T>(cur.gg * Pq.z + qk * d.z);
+            oj[3] = gdn_t<T>(cur.gg * Pq.w + qk * d.w);
+        }
+        __syncthreads();   // delta in LDS
+        const float4 d = sdv[lc];
+        const float gj = cur.gg;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+            const float kr = sk[pb][r0 + r];
+            s[r].x = gj * s[r].x + kr * d.x;
+            s[r].y = gj * s[r].y + kr * d.y;
+            s[r].z = gj * s[r].z + kr * d.z;
+            s[r].w = gj * s[r].w + kr * d.w;
+        }
+        cur = nxt;
+    }
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+        *reinterpret_cast<float4 *>(S + (int64_t)r * dv) = s[r];
+}
+
+template <typename T, int DK>
+hipError_t gdn_steps_dispatch_dv(int64_t S, int64_t B, int64_t Hk, int64_t Hv, int64_t dv,
+                                 const void *q, const void *k, const void *v, const float *g,
+                                 const float *beta, float *state, void *o, hipStream_t s)
+{
+    const int64_t ct = dv < 128 ? dv : 128;
+    const unsigned grid = (unsigned)(B * Hv * (dv / ct));
+    const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
+            *vv = static_cast<const T *>(v);
+    T *oo = static_cast<T *>(o);
+    const int n = (int)S, b = (int)B, hk = (int)Hk, hv = (int)Hv, d = (int)dv;
+    if (ct == 64)
+        gdn_steps_kernel<T, DK, 64><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv, g,
+                                                                 beta, state, oo);
+    else
+        gdn_steps_kernel<T, DK, 128><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv, g,
+                                                                  beta, state, oo);
+    return hipGetLastError();
+}
+
+template <typename T>
+hipError_t gdn_steps_dispatch(int64_t S, int64_t B, int64_t Hk, int64_t Hv, int64_t dk, int64_t dv,
+                              const void *q, const void *k, const void *v, const float *g,
+                              const float *beta, float *state, void *o, hipStream_t s)
+{
+    switch (dk) {
+    case 64: return gdn_steps_dispatch_dv<T, 64>(S, B, Hk, Hv, dv, q, k, v, g, beta, state, o, s);
+    case 128: return gdn_steps_dispatch_dv<T, 128>(S, B, Hk, Hv, dv, q, k, v, g, beta, state, o, s);
+    case 256: return gdn_steps_dispatch_dv<T, 256>(S, B, Hk, Hv, dv, q, k, v, g, beta, state, o, s);
+    default: return hipErrorInvalidValue;
+    }
+}
+
 template <typename T, int DK>
 hipError_t gdn_dispatch_dv(int64_t B, int64_t Hk, int64_t Hv, int64_t dv, const void *q,
                            const void *k, const void *v, const float *g, const float *beta,
@@ -213,6 +383,22 @@ hipError_t launch_gdn_decode(int bf16, int64_t B, int64_t Hk, int64_t Hv, int64_
     if (bf16)
         return gdn_dispatch<__bf16>(B, Hk, Hv, dk, dv, q, k, v, g, beta, state, o, s);
     return gdn_dispatch<float>(B, Hk, Hv, dk, dv, q, k, v, g, beta, state, o, s);
+}
+
+}  // namespace ssd
+
+namespace ssd {
+
+hipError_t launch_gdn_decode_steps(int bf16, int64_t S, int64_t B, int64_t Hk, int64_t Hv,
+                                   int64_t dk, int64_t dv, const void *q, const void *k,
+                                   const void *v, const float *g, const float *beta, float *state,
+                                   void *o, hipStream_t s)
+{
+    if (S == 0 || B * Hv == 0)
+        return hipSuccess;
+    if (bf16)
+        return gdn_steps_dispatch<__bf16>(S, B, Hk, Hv, dk, dv, q, k, v, g, beta, state, o, s);
+    return gdn_steps_dispatch<float>(S, B, Hk, Hv, dk, dv, q, k, v, g, beta, state, o, s);
 }
 
 }  // namespace ssd

@@ -65,6 +65,13 @@ hipError_t launch_gdn_decode(int bf16, int64_t B, int64_t Hk, int64_t Hv, int64_
                              const void *q, const void *k, const void *v, const float *g,
                              const float *beta, float *state, void *o, hipStream_t s);
 
+// S Gated DeltaNet steps in one launch, the state held in registers across
+// them: q, k [S, B, Hk, dk], v, o [S, B, Hv, dv], g, beta [S, B, Hv].
+hipError_t launch_gdn_decode_steps(int bf16, int64_t S, int64_t B, int64_t Hk, int64_t Hv,
+                                   int64_t dk, int64_t dv, const void *q, const void *k,
+                                   const void *v, const float *g, const float *beta, float *state,
+                                   void *o, hipStream_t s);
+
 // fp32 chunked scan (VALU), P <= 64, N <= 128, Q <= 256.
 hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N, int64_t G,
                            int64_t Q, const float *x, const float *dt, const float *A,

@@ -261,3 +261,23 @@ def test_gdn_validation(lib):
     assert call(gd(), (6, p(FAKE + (5 << 33) + 64))) == 4         # o inside the state
     assert call(gd(), (5, p(FAKE + (2 << 33) + 64))) == 4         # state inside v
     assert call(gd(batch=0), *[(i, None) for i in range(7)]) == 0
+
+
+def test_gdn_steps_validation(lib):
+    p = ctypes.c_void_p
+    d = ssd.SsdGdnDims(4, 16, 32, 128, 128, ssd.SSD_BF16, 0)
+    args = [p(FAKE + (k << 33)) for k in range(7)]
+
+    def call(steps, *over):
+        a = list(args)
+        for i, v in over:
+            a[i] = v
+        return lib.ssd_gdn_decode_steps(ctypes.byref(d), ctypes.c_int64(steps), *a, None)
+
+    assert call(-1) == 2
+    assert call(0, *[(i, None) for i in range(7)]) == 0
+    assert call(5, (0, None)) == 1
+    # o [S, B, Hv, dv] bf16 of 100 steps spans 100 x 32768 bytes: it reaches a
+    # state placed 2 MiB after it
+    assert call(100, (6, p(FAKE + (6 << 33))), (5, p(FAKE + (6 << 33) + (2 << 20)))) == 4
+    assert call(1 << 31) == 3

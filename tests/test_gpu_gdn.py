@@ -89,3 +89,47 @@ def test_gdn_empty_batch():
     st = torch.empty((0, 32, 128, 128), dtype=torch.float32, device="cuda")
     out = ssd.ssd_gdn_decode_step(z, z, v, g, g, st)
     assert out.shape == v.shape
+
+
+def run_steps_launch(tok, io):
+    q, k, v = dev(tok["q"], io), dev(tok["k"], io), dev(tok["v"], io)
+    state = dev(tok["state0"].copy())
+    o = ssd.ssd_gdn_decode_steps(q, k, v, dev(tok["g"]), dev(tok["beta"]), state)
+    torch.cuda.synchronize()
+    return host(o), host(state)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("batch,steps", [(1, 40), (8, 17)])
+def test_gdn_steps_page_shape(io, batch, steps):
+    """ssd_gdn_decode_steps: every step's output and the final state against the
+    oracle, and bit-identical to the same number of single-step calls (the same
+    arithmetic in the same order, the state held in registers in between)."""
+    sh = si.GDN_SHAPE
+    tok = si.gdn_tokens(500 + batch, steps, batch, sh["qk_heads"], sh["v_heads"], sh["dk"], sh["dv"], io)
+    o, s = run_steps_launch(tok, io)
+    oref, sref = oracle_run(tok, io)
+    check(o, s, oref, sref, TOL[io], f"gdn steps {io} b={batch}")
+    o1, s1 = run(tok, io, steps)
+    assert np.array_equal(o, o1) and np.array_equal(s, s1)
+
+
+@pytest.mark.parametrize("dk,dv,Hk,Hv", [(64, 64, 2, 2), (256, 64, 3, 6), (256, 256, 2, 4),
+                                         (64, 256, 1, 4)])
+def test_gdn_steps_shapes(dk, dv, Hk, Hv):
+    tok = si.gdn_tokens(dk + 3 * dv + Hk, 6, 2, Hk, Hv, dk, dv, "bf16")
+    o, s = run_steps_launch(tok, "bf16")
+    oref, sref = oracle_run(tok, "bf16")
+    check(o, s, oref, sref, TOL["bf16"], f"gdn steps dk={dk} dv={dv}")
+
+
+def test_gdn_steps_zero_steps():
+    sh = si.GDN_SHAPE
+    tok = si.gdn_tokens(9, 1, 2, sh["qk_heads"], sh["v_heads"], sh["dk"], sh["dv"], "bf16")
+    state = dev(tok["state0"].copy())
+    q = dev(tok["q"], "bf16")[:0]
+    v = dev(tok["v"], "bf16")[:0]
+    g = dev(tok["g"])[:0]
+    ssd.ssd_gdn_decode_steps(q, q, v, g, g, state)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(state), tok["state0"])
