@@ -107,7 +107,9 @@ COPY_BYTES = 1 << 30
 
 
 def _counter_means(path, counter):
-    """Per-kernel mean of one rocprofv3 counter (KiB per dispatch) and the copy total."""
+    """Per-kernel mean of one rocprofv3 counter (KiB per dispatch) over the
+    dispatches of the kernel's largest grid (the main workload's: the 2.7B
+    prefill, batch 256 for the decode kernels), and the copy total."""
     import csv
     per, copy = {}, 0.0
     for r in csv.DictReader(open(path)):
@@ -119,12 +121,17 @@ def _counter_means(path, counter):
             copy += v
         short = name.split("(")[0].split("::")[-1]
         for k in ("seg_state_kernel", "chunk_scan_kernel", "decode_rows_kernel",
-                  "decode_steps_kernel", "gdn_decode_kernel", "decode_kernel",
-                  "scan_f32_kernel"):
-            if k in short or k in name:
-                per.setdefault(k, []).append(v)
+                  "decode_steps_kernel", "gdn_decode_kernel", "gdn_steps_kernel",
+                  "decode_kernel", "scan_f32_kernel"):
+            if (k in short or k in name) and "multi" not in name:
+                per.setdefault(k, []).append((int(r["Grid_Size"]), v))
                 break
-    return {k: sum(v) / len(v) for k, v in per.items()}, copy
+    means = {}
+    for k, vals in per.items():
+        top = max(g for g, _ in vals)
+        sel = [v for g, v in vals if g == top]
+        means[k] = sum(sel) / len(sel)
+    return means, copy
 
 
 def write_traffic(fetch_csv, write_csv):
@@ -344,8 +351,9 @@ def bench_gdn(args):
 
     sh = si.GDN_SHAPE
     out = {}
-    for b in (256, 1):
-        steps = 200
+    nsteps = 200   # also in the counter runs, whose decode steps are fewer
+    for b in [b for b in (256, 1) if b in args.decode_batches]:
+        steps = nsteps
         tok = si.gdn_tokens(400 + b, steps, b, sh["qk_heads"], sh["v_heads"], sh["dk"], sh["dv"])
         q, k, v = to_dev(tok["q"], True), to_dev(tok["k"], True), to_dev(tok["v"], True)
         g, beta = to_dev(tok["g"]), to_dev(tok["beta"])
@@ -398,7 +406,7 @@ def bench_gdn(args):
     r = out[256]
     return {"workload": "ssd_gdn_decode_step, 32 value heads over 16 query/key heads, "
                         "128 x 128 fp32 state per value head (2 MB per sequence), bf16 q/k/v/o, "
-                        "200 consecutive in-place steps",
+                        f"{nsteps} consecutive in-place steps",
             "roofline": {"bound": "hbm", "kernel": "gdn_decode_kernel", "batch": 256,
                          "achieved": r["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": r["gbs"] / HBM_PEAK_GBS,
@@ -411,8 +419,8 @@ def bench_gdn(args):
                 "achieved": r["steps_launch_tflops"], "peak": FP32_VALU_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": r["steps_launch_tflops"] / FP32_VALU_PEAK_TFLOPS,
                 "flops_per_step": gdn_flops(256, sh),
-                "avg_launch_ms": r["steps_launch_ms_per_step"] * 200},
-                "note": "the same 200 steps as one ssd_gdn_decode_steps launch, the state read and "
+                "avg_launch_ms": r["steps_launch_ms_per_step"] * nsteps},
+                "note": f"the same {nsteps} steps as one ssd_gdn_decode_steps launch, the state read and "
                         "written once and held in registers across the steps"},
             "note": "batch 1 moves 2 MB per step (MALL-resident, launch-bound eager)"}
 
@@ -656,9 +664,11 @@ def main():
                                  "tflops": r["steps_launch_tflops"]}
                         for b, r in sorted(dec.items())},
         }
-        line["gdn_decode"] = bench_gdn(args)
+        if 256 in args.decode_batches:
+            line["gdn_decode"] = bench_gdn(args)
         if not args.no_cpu_baseline:
-            line["gdn_decode"]["cpu_baseline"] = cpu_baseline_gdn()
+            if "gdn_decode" in line:
+                line["gdn_decode"]["cpu_baseline"] = cpu_baseline_gdn()
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(wd)
             line["decode_steps"]["cpu_baseline"] = dict(
                 line["decode"]["cpu_baseline"],
