@@ -22,7 +22,7 @@ def _gpu_available() -> bool:
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests never fall back to anything: without a GPU they are skipped here,
-    # and on a GPU machine they fail loudly if the HIP library is missing.
+    # and on a machine with a GPU they fail loudly if the HIP library is missing.
     if _gpu_available():
         return
     skip = pytest.mark.skip(reason="no GPU visible")
