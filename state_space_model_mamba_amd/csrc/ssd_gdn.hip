@@ -166,9 +166,12 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
 // work-group keeps its tile of S in registers across all of them, so the state
 // is read once and written once per launch -- the GPU form of the page's
 // on-chip persistent state (section 2A), which turns decode from memory-bound
-// into compute-bound.  Per step the same two phases as above; q and k go
-// through LDS buffers alternating by step parity, and the next step's q, k, v,
-// g, beta are loaded into registers while the current step computes.
+// into compute-bound.  Per step the same arithmetic as above, with two
+// barriers: every thread sums the waves' partials for its own four columns and
+// forms their delta itself (the first LPR threads also store o), so no third
+// hand-off is needed.  q and k go through LDS buffers alternating by step
+// parity, and the next step's q, k, v, g, beta are loaded into registers while
+// the current step computes.
 // q, k [S, B, Hk, DK], v, o [S, B, Hv, dv], g, beta [S, B, Hv].
 template <typename T, int DK, int CT>
 __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
@@ -181,7 +184,6 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
     constexpr int QK = DK / kGdnThreads > 0 ? DK / kGdnThreads : 1;   // q/k elements per thread
     __shared__ float sk[2][DK], sq[2][DK];
     __shared__ float4 part[4 * RPI][LPR][2];
-    __shared__ float4 sdv[LPR];
     __shared__ float sqk;
 
     const int tiles = dv / CT;
@@ -204,7 +206,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
         s[r] = *reinterpret_cast<const float4 *>(S + (int64_t)r * dv);
 
     // step t's inputs as this thread needs them (q/k: its share for the LDS
-    // copy; v, g, beta: only the first LPR threads form the delta)
+    // copy; v of its four columns; g, beta)
     struct In {
         float qv[QK], kv[QK], vv[4], gg, bb;
     };
@@ -216,11 +218,9 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
             in.qv[e] = idx < DK ? gdn_f<T>(qb[tt * qks + idx]) : 0.f;
             in.kv[e] = idx < DK ? gdn_f<T>(kb[tt * qks + idx]) : 0.f;
         }
-        if (tid < LPR) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                in.vv[e] = gdn_f<T>(vb[tt * vs + e]);
-        }
+        for (int e = 0; e < 4; ++e)
+            in.vv[e] = gdn_f<T>(vb[tt * vs + e]);
         in.gg = g[tt * gs + bj];
         in.bb = beta[tt * gs + bj];
     };
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
             }
         }
         fetch(nxt, t + 1);
-        __syncthreads();   // q, k of step t in LDS; last step's delta consumed
+        __syncthreads();   // q, k of step t in LDS; last step's partials consumed
         float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), pp = pr;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -260,20 +260,19 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
                 sqk = d;
         }
         __syncthreads();   // partials and q . k in LDS
-        if (tid < LPR) {
-            float4 R = part[0][tid][0], Pq = part[0][tid][1];
+        float4 R = part[0][lc][0], Pq = part[0][lc][1];
 #pragma unroll
-            for (int m = 1; m < 4 * RPI; ++m) {
-                const float4 a = part[m][tid][0], c = part[m][tid][1];
-                R.x += a.x; R.y += a.y; R.z += a.z; R.w += a.w;
-                Pq.x += c.x; Pq.y += c.y; Pq.z += c.z; Pq.w += c.w;
-            }
-            float4 d;
-            d.x = cur.bb * (cur.vv[0] - cur.gg * R.x);
-            d.y = cur.bb * (cur.vv[1] - cur.gg * R.y);
-            d.z = cur.bb * (cur.vv[2] - cur.gg * R.z);
-            d.w = cur.bb * (cur.vv[3] - cur.gg * R.w);
-            sdv[tid] = d;
+        for (int m = 1; m < 4 * RPI; ++m) {
+            const float4 a = part[m][lc][0], c = part[m][lc][1];
+            R.x += a.x; R.y += a.y; R.z += a.z; R.w += a.w;
+            Pq.x += c.x; Pq.y += c.y; Pq.z += c.z; Pq.w += c.w;
+        }
+        float4 d;
+        d.x = cur.bb * (cur.vv[0] - cur.gg * R.x);
+        d.y = cur.bb * (cur.vv[1] - cur.gg * R.y);
+        d.z = cur.bb * (cur.vv[2] - cur.gg * R.z);
+        d.w = cur.bb * (cur.vv[3] - cur.gg * R.w);
+        if (tid < LPR) {
             T *oj = ob + (int64_t)t * vs;
             const float qk = sqk;
             oj[0] = gdn_t<T>(cur.gg * Pq.x + qk * d.x);
@@ -281,8 +280,6 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
             oj[2] = gdn_t<T>(cur.gg * Pq.z + qk * d.z);
             oj[3] = gdn_t<T>(cur.gg * Pq.w + qk * d.w);
         }
-        __syncthreads();   // delta in LDS
-        const float4 d = sdv[lc];
         const float gj = cur.gg;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
