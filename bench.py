@@ -39,10 +39,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s (256 CU x 2.4 GHz x 256 FLOP/clk)
 METRIC = "SSD prefill tokens/s (MFMA %) + decode steps/s (HBM GB/s %) at 2.7B-layer shape"
-KERNEL_SOURCES = ["state_space_model_mamba_amd/csrc/ssd_scan_bf16.hip",
-                  "state_space_model_mamba_amd/csrc/ssd_decode.hip",
-                  "state_space_model_mamba_amd/csrc/ssd_decode_steps.hip",
-                  "state_space_model_mamba_amd/csrc/ssd_gdn.hip"]
+CSRC = "state_space_model_mamba_amd/csrc/"
+# the source of each measured kernel; its counters in profiles/traffic.json are
+# used while that file and the shared header are unchanged
+KERNEL_SOURCE = {"seg_state_kernel": "ssd_scan_bf16.hip", "chunk_scan_kernel": "ssd_scan_bf16.hip",
+                 "decode_rows_kernel": "ssd_decode.hip", "decode_kernel": "ssd_decode.hip",
+                 "decode_steps_kernel": "ssd_decode_steps.hip",
+                 "gdn_decode_kernel": "ssd_gdn.hip", "gdn_steps_kernel": "ssd_gdn.hip",
+                 "scan_f32_kernel": "ssd_scan_f32.hip"}
 
 
 def prefill_bytes(w) -> int:
@@ -79,10 +83,11 @@ def decode_steps_flops(b, w) -> int:
     return rows * (5 * w.dstate + 3)
 
 
-def source_digest() -> str:
+def source_digest(kernel: str) -> str:
+    """sha256 of the kernel's source file and the shared kernel header."""
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, f), "rb") as fh:
+    for f in (KERNEL_SOURCE[kernel], "ssd_kernels.h"):
+        with open(os.path.join(ROOT, CSRC, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()
 
@@ -92,10 +97,8 @@ def committed_traffic(kernel: str):
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    if rec.get("source_sha256") != source_digest():
-        return None
     k = rec.get("kernels", {}).get(kernel)
-    if not k:
+    if not k or k.get("source_sha256") != source_digest(kernel):
         return None
     return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
             "total_bytes": k["fetch_bytes"] + k["write_bytes"], "scale": rec.get("copy_scale"),
@@ -143,9 +146,9 @@ def write_traffic(fetch_csv, write_csv):
     if fcopy <= 0 or wcopy <= 0:
         raise SystemExit("no copy-calibration dispatches in the counter files")
     fs, ws = COPY_BYTES / (fcopy * 1024), COPY_BYTES / (wcopy * 1024)
-    rec = {"source_sha256": source_digest(), "copy_bytes": COPY_BYTES,
-           "copy_scale": {"fetch": fs, "write": ws},
-           "kernels": {k: {"fetch_bytes": fetch[k] * 1024 * fs,
+    rec = {"copy_bytes": COPY_BYTES, "copy_scale": {"fetch": fs, "write": ws},
+           "kernels": {k: {"source_sha256": source_digest(k),
+                           "fetch_bytes": fetch[k] * 1024 * fs,
                            "write_bytes": write.get(k, 0.0) * 1024 * ws,
                            "fetch_kib_raw": fetch[k], "write_kib_raw": write.get(k, 0.0)}
                        for k in fetch}}
