@@ -155,9 +155,11 @@ ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const float *dt, 
  *   final_states [S,H,P,N] fp32                   output (may alias initial_states)
  *   workspace : >= ssd_chunk_scan_varlen_workspace_size bytes
  * Zero-length sequences pass their state through.  Consecutive sequences of
- * equal length run as one batched scan, so a batch of equal lengths costs one
- * call; every run is validated before the first is enqueued.  Supported shapes
- * and the alignment of each sequence's slices as for ssd_chunk_scan.
+ * equal length form one run, laid out like a batched scan; with bf16 I/O up
+ * to eight runs share one launch of each scan kernel (the workspace holds a
+ * region per run), with fp32 I/O each run is one scan call.  Every run is
+ * validated before anything is enqueued.  Supported shapes and the alignment
+ * of each sequence's slices as for ssd_chunk_scan.
  */
 ssd_status ssd_chunk_scan_varlen_workspace_size(const ssd_dims *dims, const int64_t *cu_seqlens,
                                                 size_t *bytes);
