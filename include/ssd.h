@@ -1,6 +1,9 @@
 /*
  * ssd.h -- C ABI of libssd: the Mamba-2 state-space-duality (SSD) layer on one
- * AMD Instinct MI355X (gfx950): chunked prefill scan and O(1) cached decode.
+ * AMD Instinct MI355X (gfx950): chunked prefill scan (also over packed batches
+ * of different lengths), O(1) cached decode (one step, or many known steps in
+ * one launch with the state on-chip), an optional fused step-size prep, and
+ * the Gated DeltaNet decode step of the FPGA decode page (ssd_gdn_*).
  *
  * The operation.  "Compiler-First State Space Duality and Portable O(1)
  * Autoregressive Caching for Inference" (section 2, methodology) describes
@@ -20,8 +23,10 @@
  * for t = 1..L with the chunked (state-space-duality) algorithm: inside each
  * chunk of Q tokens a causal quadratic form, across chunks a state passed from
  * chunk to chunk.  ssd_decode_step is exactly one more step t on the cached
- * state.  dt is taken as given (already softplus-ed, positive); A should be
- * <= 0 (A > 0 is not rejected, but exp(dt*A) may overflow and is unsupported).
+ * state, ssd_decode_steps S of them.  dt is taken as given (already
+ * softplus-ed, positive) unless ssd_dims.flags has SSD_DT_SOFTPLUS; A should
+ * be <= 0 (A > 0 is not rejected, but exp(dt*A) may overflow and is
+ * unsupported).
  *
  * Conventions shared by every call:
  *   - Every tensor pointer is a DEVICE pointer to contiguous row-major memory
@@ -32,8 +37,8 @@
  *   - Arguments are validated before any device call; on an error nothing is
  *     launched and a status code is returned.  No call aborts or throws.
  *   - Alignment: x, B, C, y and the state / workspace buffers must be 16-byte
- *     aligned (x and y of ssd_decode_step: element-aligned); dt, A, D 4-byte.
- *     Otherwise SSD_ERR_ALIGNMENT.
+ *     aligned (x and y of ssd_decode_step(s): element-aligned); dt, A, D
+ *     4-byte.  Otherwise SSD_ERR_ALIGNMENT.
  *   - Float inputs must be finite.  Outputs for non-finite inputs are undefined.
  *   - The library holds no global state; calls on different streams may run
  *     concurrently if their buffers do not overlap.
