@@ -13,6 +13,10 @@ step is launch-bound).  ``decode_steps`` runs the same 1000 steps as one
 ssd_decode_steps launch (state held on-chip across the steps), whose bound is
 fp32 VALU arithmetic.
 
+The defaults (100 warm-up steps, 100 timed) matter: the GPU's clock ramps up
+over the first ~20 ms of back-to-back work, and a prefill step is 0.3 ms, so a
+short warm-up times the ramp rather than the sustained rate.
+
 Prints ONE JSON line.  ``roofline`` is the dominant prefill kernel
 (chunk_scan_kernel): algorithmic bytes of the layer per launch / its average
 launch time measured with HIP events on the launch stream; ``decode.roofline``
@@ -561,8 +565,8 @@ def cpu_baseline_gdn(nseq=32, steps=40, batch=256):
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--decode-batches", type=str, default="256,64,16,1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
