@@ -812,12 +812,15 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
 // LDS slots (buffer loads with an LDS destination, no registers in between),
 // two tiles ahead of the one being computed, with one barrier per tile.
 // Four heads per work-group share each B tile; wave w = (head w / 2, P half
-// w % 2) loads half of its own head's x tile.
+// w % 2) loads half of its own head's x tile, and the step sizes of 8 tokens
+// for all four heads (16 contiguous bytes per token: one cache line per token,
+// not one per token and wave).
 constexpr int kStHeads = 4, kStWaves = 2 * kStHeads, kStThreads = 64 * kStWaves;
 constexpr int kStBBlocks = kT * kBRow / 1024 / kStWaves;   // 1 KB B blocks per wave per tile
 constexpr int kStXBlocks = kT * kXRow / 1024 / 2;          // 1 KB x blocks per wave per tile
 constexpr int kStLoads = kStBBlocks + kStXBlocks + 1;      // memory instructions per wave per tile (+ dt)
-constexpr size_t kStSmemBytes = 3 * (size_t)kT * (kBRow + kStHeads * kXRow + kStWaves * 4) + (size_t)kStWaves * kT * 4;
+constexpr size_t kStSmemBytes = 3 * (size_t)kT * (kBRow + kStHeads * kXRow + kStHeads * 4) + (size_t)kStWaves * kT * 4;
+static_assert(kStWaves * 8 == kT && kStHeads == 4, "each wave loads the dt of 8 tokens x 4 heads");
 
 struct StIo {
     const __bf16 *B, *x;       // this (b, group) / (b, head) at token 0
@@ -826,6 +829,7 @@ struct StIo {
     unsigned boff[kStBBlocks]; // this lane's source offset within a tile, per block
     unsigned xoff[kStXBlocks];
     unsigned doff;
+    unsigned dbytes;           // bytes of dt per token for this quad's heads (4 per head)
 };
 
 // Buffer resource words over the valid rows of a tile (as tile_rsrc), for
@@ -878,8 +882,9 @@ __device__ __forceinline__ void st_issue(const StIo &io, unsigned Bslot, unsigne
 #pragma unroll
     for (int k = 0; k < kStXBlocks; ++k)
         lds_load16(Xslot + 1024 * (kStXBlocks * (w & 1) + k), rx, io.xoff[k]);
-    const u32x4 rd = tile_words(io.dt + t0 * (io.dp / 4), rows, (unsigned)io.dp, 4);
-    lds_load4(Dslot, rd, io.doff);
+    const u32x4 rd = tile_words(io.dt + t0 * (io.dp / 4), rows, (unsigned)io.dp, io.dbytes);
+    if ((threadIdx.x & 63) < 32)
+        lds_load4(Dslot + 128 * w, rd, io.doff);
 }
 
 // The LDS location at byte address a, as a pointer.
@@ -901,12 +906,16 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
     __shared__ __align__(16) unsigned char sB0[kT * kBRow], sB1[kT * kBRow], sB2[kT * kBRow];
     __shared__ __align__(16) unsigned char sX0[kStHeads][kT * kXRow], sX1[kStHeads][kT * kXRow],
         sX2[kStHeads][kT * kXRow];
-    __shared__ __align__(16) unsigned char sD0[kStWaves][kT * 4], sD1[kStWaves][kT * 4], sD2[kStWaves][kT * 4];
+    __shared__ __align__(16) unsigned char sD0[kT * kStHeads * 4], sD1[kT * kStHeads * 4], sD2[kT * kStHeads * 4];
     __shared__ __align__(16) float swd[kStWaves][kT];
 
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     const int hs = w >> 1, ph = w & 1;
-    const int64_t j = xcd_remap(bid, nblk);
+    // Work-groups in dispatch order, without the XCD remap of the scan kernel:
+    // the head quads of one token range then run on different XCDs, which
+    // streams x faster (B, shared by the quads, is small and comes from the
+    // memory-side cache).
+    const int64_t j = bid;
     const int nquad = a.G * a.nq;
     const int quad = (int)(j % nquad);
     const int64_t r = j / nquad;
@@ -943,7 +952,9 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
     io.dp = (int64_t)a.H * 4;
     io.B = a.B + (b * L * a.G + grp) * kN;
     io.x = a.x + (b * L * a.H + h) * kP;
-    io.dt = a.dt + b * L * a.H + h;
+    const int hq = (quad % a.nq) * kStHeads;               // the quad's first head in the group
+    io.dt = a.dt + b * L * a.H + grp * a.hg + hq;
+    io.dbytes = 4u * (unsigned)std::min(kStHeads, a.hg - hq);
 #pragma unroll
     for (int k = 0; k < kStBBlocks; ++k) {
         const int row = 4 * (kStBBlocks * w + k) + (l >> 4), pc = l & 15;
@@ -954,7 +965,8 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
         const int row = 8 * (kStXBlocks * ph + k) + (l >> 3), pc = l & 7;
         io.xoff[k] = (unsigned)row * (unsigned)io.xp + (unsigned)((pc ^ xswz(row)) << 4);
     }
-    io.doff = (unsigned)l * (unsigned)io.dp;
+    // lanes 0..31 of wave w: token 8 w + l / 4, head l % 4 of the quad
+    io.doff = (unsigned)(8 * w + (l >> 2)) * (unsigned)io.dp + 4u * (unsigned)(l & 3);
 
     // Zero the ring once: rows past a unit's end then hold zeros or an older
     // tile's finite values, which its zero weights cancel.
@@ -983,7 +995,7 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
     (unsigned)reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) unsigned char *)(p)))
     const unsigned aB0 = SSD_LDS(sB0), aB1 = SSD_LDS(sB1), aB2 = SSD_LDS(sB2);
     const unsigned aX0 = SSD_LDS(&sX0[hs][0]), aX1 = SSD_LDS(&sX1[hs][0]), aX2 = SSD_LDS(&sX2[hs][0]);
-    const unsigned aD0 = SSD_LDS(&sD0[w][0]), aD1 = SSD_LDS(&sD1[w][0]), aD2 = SSD_LDS(&sD2[w][0]);
+    const unsigned aD0 = SSD_LDS(sD0), aD1 = SSD_LDS(sD1), aD2 = SSD_LDS(sD2);
 #undef SSD_LDS
     st_issue(io, aB0, aX0, aD0, tseg0, tseg1, w);
     st_issue(io, aB1, aX1, aD1, tseg0 + kT, tseg1, w);
@@ -995,7 +1007,7 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
         lds_barrier();                            // ... and every wave's; slot of t0 - kT free
         st_issue(io, Bn, Xn, Dn, t0 + 2 * kT, tseg1, w);
         const unsigned char *Bs = lds_ptr(aB), *Xs = lds_ptr(aX), *Ds = lds_ptr(aD);
-        float dtc = reinterpret_cast<const float *>(Ds)[l];
+        float dtc = reinterpret_cast<const float *>(Ds)[kStHeads * l + hs];
         if constexpr (kSp)   // the step size from u; tokens past the end keep 0
             dtc = l < tseg1 - t0 ? softplus_dt(dtc, dtb) : 0.f;
         const float lam = wave_inclusive_sum(dtc * Ah2, l);
