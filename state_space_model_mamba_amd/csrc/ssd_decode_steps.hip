@@ -154,16 +154,6 @@ __device__ __forceinline__ float partner(float v)
         return dpp<0x140>(v);
 }
 
-// Sum of the two results of a lane-swap builtin.  When one instruction read
-// both results directly, hipcc (ROCm 7.2) emitted it reading the first result
-// twice; passing the second through an empty asm statement keeps them apart.
-__device__ __forceinline__ float swap_sum(u32x2 s)
-{
-    unsigned second = s[1];
-    asm volatile("" : "+v"(second));
-    return __builtin_bit_cast(float, s[0]) + __builtin_bit_cast(float, second);
-}
-
 // Halving exchange on lane bit kBit: a lane whose bit is 0 keeps row `lo`,
 // one whose bit is 1 keeps `hi`, each summed with the partner lane's value.
 template <int kBit>
@@ -175,7 +165,7 @@ __device__ __forceinline__ float halve(float lo, float hi, int lane)
                                                __builtin_bit_cast(unsigned, hi), false, false)
             : __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, lo),
                                                __builtin_bit_cast(unsigned, hi), false, false);
-        return swap_sum(s);
+        return swap_sum(s[0], s[1]);   // (ssd_kernels.h)
     } else {
         const bool up = (lane >> kBit) & 1;
         const float mine = up ? hi : lo, send = up ? lo : hi;
@@ -188,10 +178,7 @@ template <int kBit>
 __device__ __forceinline__ float pair_sum(float v)
 {
     if constexpr (kBit >= 4) {
-        const unsigned u = __builtin_bit_cast(unsigned, v);
-        const u32x2 s = kBit == 5 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
-                                  : __builtin_amdgcn_permlane16_swap(u, u, false, false);
-        return swap_sum(s);
+        return lane_pair_sum<kBit>(v);
     } else {
         return v + partner<kBit>(v);
     }

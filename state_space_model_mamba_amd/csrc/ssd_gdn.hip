@@ -167,14 +167,29 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
 // is read once and written once per launch -- the GPU form of the page's
 // on-chip persistent state (section 2A), which turns decode from memory-bound
 // into compute-bound.  Per step the same arithmetic as above, with two
-// barriers: every thread sums the waves' partials for its own four columns and
-// forms their delta itself (the first LPR threads also store o), so no third
-// hand-off is needed.  q and k go through LDS buffers alternating by step
-// parity, and the next step's q, k, v, g, beta are loaded into registers while
-// the current step computes.
+// barriers: a wave first sums its row groups' partials across lanes (lane
+// swaps), then every thread sums the four waves' partials for its own four
+// columns and forms their delta itself (the first LPR threads also store o),
+// so no third hand-off is needed.  q and k go through LDS buffers alternating
+// by step parity, and the next step's q, k, v, g, beta are loaded into
+// registers while the current step computes.
+//
+// The registers hold S / sc, sc being the product of the gates since the last
+// renormalisation: a step is then one fused multiply-add per element,
+// S / sc' += k (dv / sc'), with sc' = sc g, instead of a multiply by g and a
+// multiply-add; the retrieval and readout are scaled by sc after the
+// reduction.  A step that would take sc' outside [2^-64, 2^64] (g = 0
+// included) multiplies the registers by sc' and restarts sc at 1.  g is one
+// value per work-group and step, so the test is uniform.  1 / sc' is the
+// hardware reciprocal (within 1 ulp).
 // q, k [S, B, Hk, DK], v, o [S, B, Hv, dv], g, beta [S, B, Hv].
+// Occupancy: a thread holds DK * CT / 256 state elements.  At 64 (dk = dv =
+// 128) the kernel is held to four waves per SIMD (128 VGPRs; the compiler
+// alone took 160 and three waves, 18% slower at batch 256 with no spill inside
+// the step loop); larger slices are left to the compiler.
 template <typename T, int DK, int CT>
-__global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
+__global__ __launch_bounds__(kGdnThreads) __attribute__((amdgpu_waves_per_eu(DK * CT <= 128 * 128 ? 4 : 1)))
+void gdn_steps_kernel(
     int nsteps, int Bn, int Hk, int Hv, int dv, const T *__restrict__ q,
     const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, float *__restrict__ state, T *__restrict__ o)
@@ -183,7 +198,8 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
     static_assert(ROWS >= 1 && ROWS * 4 * RPI == DK, "DK rows split over 4 waves x RPI");
     constexpr int QK = DK / kGdnThreads > 0 ? DK / kGdnThreads : 1;   // q/k elements per thread
     __shared__ float sk[2][DK], sq[2][DK];
-    __shared__ float4 part[4 * RPI][LPR][2];
+    __shared__ float4 part[4][LPR][2];   // per wave: r (row group 0) and p (row group 1)
+    static_assert(RPI == 2 || RPI == 4, "row groups of a wave on lane bit 5 (and 4)");
     __shared__ float sqk;
 
     const int tiles = dv / CT;
@@ -227,6 +243,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
 
     In cur, nxt;
     fetch(cur, 0);
+    float sc = 1.f;
     for (int t = 0; t < nsteps; ++t) {
         const int pb = t & 1;
 #pragma unroll
@@ -246,8 +263,22 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
             pr.x += kr * s[r].x; pr.y += kr * s[r].y; pr.z += kr * s[r].z; pr.w += kr * s[r].w;
             pp.x += qr * s[r].x; pp.y += qr * s[r].y; pp.z += qr * s[r].z; pp.w += qr * s[r].w;
         }
-        part[w * RPI + lg][lc][0] = pr;
-        part[w * RPI + lg][lc][1] = pp;
+        // the wave's RPI row groups (lane bits 4 and 5) summed in every lane;
+        // lanes of row group 0 store the retrieval, row group 1 the readout
+        auto wave_sum = [&](float4 &v) {
+            if constexpr (RPI == 4) {
+                v.x = lane_pair_sum<4>(v.x); v.y = lane_pair_sum<4>(v.y);
+                v.z = lane_pair_sum<4>(v.z); v.w = lane_pair_sum<4>(v.w);
+            }
+            v.x = lane_pair_sum<5>(v.x); v.y = lane_pair_sum<5>(v.y);
+            v.z = lane_pair_sum<5>(v.z); v.w = lane_pair_sum<5>(v.w);
+        };
+        wave_sum(pr);
+        wave_sum(pp);
+        if (lg == 0)
+            part[w][lc][0] = pr;
+        else if (lg == 1)
+            part[w][lc][1] = pp;
         if (w == 1) {   // q . k (wave 1, so wave 0 is free for the delta below)
             float d = 0.f;
 #pragma unroll
@@ -262,11 +293,13 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
         __syncthreads();   // partials and q . k in LDS
         float4 R = part[0][lc][0], Pq = part[0][lc][1];
 #pragma unroll
-        for (int m = 1; m < 4 * RPI; ++m) {
+        for (int m = 1; m < 4; ++m) {
             const float4 a = part[m][lc][0], c = part[m][lc][1];
             R.x += a.x; R.y += a.y; R.z += a.z; R.w += a.w;
             Pq.x += c.x; Pq.y += c.y; Pq.z += c.z; Pq.w += c.w;
         }
+        R.x *= sc; R.y *= sc; R.z *= sc; R.w *= sc;
+        Pq.x *= sc; Pq.y *= sc; Pq.z *= sc; Pq.w *= sc;
         float4 d;
         d.x = cur.bb * (cur.vv[0] - cur.gg * R.x);
         d.y = cur.bb * (cur.vv[1] - cur.gg * R.y);
@@ -280,20 +313,31 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_steps_kernel(
             oj[2] = gdn_t<T>(cur.gg * Pq.z + qk * d.z);
             oj[3] = gdn_t<T>(cur.gg * Pq.w + qk * d.w);
         }
-        const float gj = cur.gg;
+        float scn = sc * cur.gg;
+        if (__builtin_amdgcn_readfirstlane(!(scn >= 0x1p-64f && scn <= 0x1p64f))) {
+#pragma unroll
+            for (int r = 0; r < ROWS; ++r) {
+                s[r].x *= scn; s[r].y *= scn; s[r].z *= scn; s[r].w *= scn;
+            }
+            scn = 1.f;
+        }
+        sc = scn;
+        const float ri = __builtin_amdgcn_rcpf(scn);
+        d.x *= ri; d.y *= ri; d.z *= ri; d.w *= ri;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
             const float kr = sk[pb][r0 + r];
-            s[r].x = gj * s[r].x + kr * d.x;
-            s[r].y = gj * s[r].y + kr * d.y;
-            s[r].z = gj * s[r].z + kr * d.z;
-            s[r].w = gj * s[r].w + kr * d.w;
+            s[r].x = __builtin_fmaf(kr, d.x, s[r].x);
+            s[r].y = __builtin_fmaf(kr, d.y, s[r].y);
+            s[r].z = __builtin_fmaf(kr, d.z, s[r].z);
+            s[r].w = __builtin_fmaf(kr, d.w, s[r].w);
         }
         cur = nxt;
     }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r)
-        *reinterpret_cast<float4 *>(S + (int64_t)r * dv) = s[r];
+        *reinterpret_cast<float4 *>(S + (int64_t)r * dv) =
+            make_float4(s[r].x * sc, s[r].y * sc, s[r].z * sc, s[r].w * sc);
 }
 
 template <typename T, int DK>
@@ -301,7 +345,10 @@ hipError_t gdn_steps_dispatch_dv(int64_t S, int64_t B, int64_t Hk, int64_t Hv, i
                                  const void *q, const void *k, const void *v, const float *g,
                                  const float *beta, float *state, void *o, hipStream_t s)
 {
-    const int64_t ct = dv < 128 ? dv : 128;
+    // 64-column tiles at dk = 256, so that a thread holds 64 state elements
+    // and the kernel runs four waves per SIMD (128-column tiles: 128 elements,
+    // 256 VGPRs, one wave)
+    const int64_t ct = (dv < 128 || DK == 256) ? 64 : 128;
     const unsigned grid = (unsigned)(B * Hv * (dv / ct));
     const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
             *vv = static_cast<const T *>(v);

@@ -43,6 +43,26 @@ __device__ __forceinline__ float softplus_dt(float u, float bias)
     return fmaxf(v, 0.f) + l;
 }
 
+// Sum of a wave value with its partner lane across lane bit 4 or 5 (the lane
+// 16 or 32 away), every lane keeping the sum: one permlane swap and one add.
+// When one instruction read both results of the swap builtin directly, hipcc
+// (ROCm 7.2) emitted it reading the first result twice; passing the second
+// through an empty asm statement keeps them apart.
+__device__ __forceinline__ float swap_sum(unsigned first, unsigned second)
+{
+    asm volatile("" : "+v"(second));
+    return __builtin_bit_cast(float, first) + __builtin_bit_cast(float, second);
+}
+template <int kBit>
+__device__ __forceinline__ float lane_pair_sum(float v)
+{
+    static_assert(kBit == 4 || kBit == 5, "lane bit 4 or 5");
+    const unsigned u = __builtin_bit_cast(unsigned, v);
+    const auto s = kBit == 5 ? __builtin_amdgcn_permlane32_swap(u, u, false, false)
+                             : __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    return swap_sum(s[0], s[1]);
+}
+
 // state[i] = src ? src[i] : 0 for i < n (fill/copy kernel, graph-capturable).
 hipError_t launch_state_init(float *state, const float *src, int64_t n, hipStream_t s);
 
