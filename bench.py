@@ -481,6 +481,112 @@ def bench_varlen(args):
             "runs_of_equal_length": runs, "kernel_launches": 2 * ((runs + 7) // 8)}
 
 
+NONCACHED_CONTEXTS = (256, 1024, 4096, 16384, 32768)
+NONCACHED_NEW = 64
+
+
+def bench_noncached(args):
+    """Cached against non-cached generation on one 2.7B-shaped layer (80 heads x
+    64, dstate 128, 1 group, chunk 256), batch 1, bf16 tokens: the comparison of
+    the Compiler-First page's evaluation (section 4) on one layer.  Non-cached:
+    each new token re-runs ssd_chunk_scan over the prefix and the token from a
+    zero state (the token's output is the last row); cached: ssd_chunk_scan over
+    the prefix once, then one ssd_decode_step per token on the carried state.
+    For each context length: the time per token of both, the decode step timed on
+    the state that the prefill of that context produced (eager and replayed from
+    a captured graph), and the time to generate NONCACHED_NEW tokens after the
+    prompt both ways."""
+    import torch
+
+    import ssd_inputs as si
+    import state_space_model_mamba_amd as ssd
+
+    top = max(NONCACHED_CONTEXTS) + NONCACHED_NEW
+    w = si.small_workload("noncached_2p7b", batch=1, seqlen=top, nheads=80, headdim=64,
+                          dstate=128, ngroups=1, chunk=256, seed=410)
+    A, D = si.head_params(w)
+    inp = si.prefill_inputs(w)
+    x, dt = to_dev(inp["x"], True), to_dev(inp["dt"])
+    B, C = to_dev(inp["B"], True), to_dev(inp["C"], True)
+    del inp
+    dA, dD = to_dev(A), to_dev(D)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+    def scan(n):                      # batch 1: the first n tokens are a contiguous prefix
+        return ssd.ssd_chunk_scan(x[:, :n], dt[:, :n], dA, B[:, :n], C[:, :n], dD, w.chunk)
+
+    def timed(fn, reps):
+        fn()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(reps):
+            fn()
+        e1.record()
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    def decode(state, t):
+        return ssd.ssd_decode_step(x[:, t], dt[:, t], dA, B[:, t], C[:, t], dD, state)
+
+    rows = []
+    for ctx in NONCACHED_CONTEXTS:
+        nc_ms = timed(lambda: scan(ctx + 1), 10)
+        pre_ms = timed(lambda: scan(ctx), 10)
+        _, state = scan(ctx)
+        decode(state.clone(), ctx)           # warm-up on a copy
+        st = state.clone()
+        torch.cuda.synchronize()
+        e0.record()
+        for i in range(NONCACHED_NEW):
+            decode(st, ctx + i)
+        e1.record()
+        torch.cuda.synchronize()
+        dec_ms = e0.elapsed_time(e1) / NONCACHED_NEW
+        st = state.clone()
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                for i in range(NONCACHED_NEW):
+                    decode(st, ctx + i)
+        torch.cuda.current_stream().wait_stream(side)
+        graph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        graph.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        gdec_ms = e0.elapsed_time(e1) / NONCACHED_NEW
+        del graph
+        # NONCACHED_NEW tokens after the prompt, both ways
+        e0.record()
+        for i in range(NONCACHED_NEW):
+            scan(ctx + i + 1)
+        e1.record()
+        torch.cuda.synchronize()
+        gen_nc = e0.elapsed_time(e1)
+        e0.record()
+        _, st = scan(ctx)
+        for i in range(NONCACHED_NEW):
+            decode(st, ctx + i)
+        e1.record()
+        torch.cuda.synchronize()
+        gen_c = e0.elapsed_time(e1)
+        rows.append({"context": ctx, "noncached_ms_per_token": nc_ms, "prefill_ms": pre_ms,
+                     "cached_ms_per_token": dec_ms, "cached_graph_ms_per_token": gdec_ms,
+                     f"generate_{NONCACHED_NEW}_noncached_ms": gen_nc,
+                     f"generate_{NONCACHED_NEW}_cached_ms": gen_c,
+                     "cached_tokens_per_s": 1e3 / dec_ms, "noncached_tokens_per_s": 1e3 / nc_ms})
+    del x, dt, B, C
+    torch.cuda.empty_cache()
+    return {"workload": "one Mamba-2-2.7B-shaped layer (80 heads x 64, dstate 128, 1 group, "
+                        "chunk 256), batch 1, bf16 tokens; non-cached = ssd_chunk_scan over "
+                        "the prefix and the token for every token, cached = one "
+                        "ssd_chunk_scan over the prompt, then ssd_decode_step per token",
+            "rows": rows}
+
+
 def cpu_baseline_prefill(w, npairs=None):
     """The fp64 oracle on `npairs` of the layer's (batch, head) sequences, full
     length each, threaded over pairs; tokens/s scaled to the whole layer."""
@@ -633,6 +739,7 @@ def main():
     }
     if not args.no_extras:
         line["prefill_varlen"] = bench_varlen(args)
+        line["noncached_vs_cached"] = bench_noncached(args)
     if not args.no_decode:
         wd, dec = bench_decode(args)
         main_b = max(dec)
