@@ -678,8 +678,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
-                    help="skip the fused-softplus and mixed-length prefill timings (counter runs: "
-                         "every dispatch of a kernel is then the main workload's)")
+                    help="skip the fused-softplus, mixed-length and non-cached timings (counter "
+                         "and trace runs: every dispatch of a kernel is then the main workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
     ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
