@@ -166,13 +166,12 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
 // work-group keeps its tile of S in registers across all of them, so the state
 // is read once and written once per launch -- the GPU form of the page's
 // on-chip persistent state (section 2A), which turns decode from memory-bound
-// into compute-bound.  Per step the same arithmetic as above, with two
-// barriers: a wave first sums its row groups' partials across lanes (lane
-// swaps), then every thread sums the four waves' partials for its own four
-// columns and forms their delta itself (the first LPR threads also store o),
-// so no third hand-off is needed.  q and k go through LDS buffers alternating
-// by step parity, and the next step's q, k, v, g, beta are loaded into
-// registers while the current step computes.
+// into compute-bound.  Per step the same arithmetic as above, with one
+// barrier: a wave first sums its row groups' partials across lanes (lane
+// swaps) and stores them, and after the barrier every thread sums the four
+// waves' partials for its own four columns and forms their delta itself (the
+// first LPR threads also store o).  q and k reach LDS a step ahead of their
+// use, through three buffers; the partials alternate between two.
 //
 // The registers hold S / sc, sc being the product of the gates since the last
 // renormalisation: a step is then one fused multiply-add per element,
@@ -197,10 +196,12 @@ void gdn_steps_kernel(
     constexpr int LPR = CT / 4, RPI = 64 / LPR, ROWS = DK / (4 * RPI);
     static_assert(ROWS >= 1 && ROWS * 4 * RPI == DK, "DK rows split over 4 waves x RPI");
     constexpr int QK = DK / kGdnThreads > 0 ? DK / kGdnThreads : 1;   // q/k elements per thread
-    __shared__ float sk[2][DK], sq[2][DK];
-    __shared__ float4 part[4][LPR][2];   // per wave: r (row group 0) and p (row group 1)
+    // q and k in three buffers (step t reads t % 3 and writes step t + 1's
+    // into the next); the partials and q . k in two (by step parity)
+    __shared__ float sk[3][DK], sq[3][DK];
+    __shared__ float4 part[2][4][LPR][2];   // per wave: r (row group 0) and p (row group 1)
     static_assert(RPI == 2 || RPI == 4, "row groups of a wave on lane bit 5 (and 4)");
-    __shared__ float sqk;
+    __shared__ float sqk[2];
 
     const int tiles = dv / CT;
     const int bj = blockIdx.x / tiles, tile = blockIdx.x - bj * tiles;
@@ -221,12 +222,16 @@ void gdn_steps_kernel(
     for (int r = 0; r < ROWS; ++r)
         s[r] = *reinterpret_cast<const float4 *>(S + (int64_t)r * dv);
 
-    // step t's inputs as this thread needs them (q/k: its share for the LDS
-    // copy; v of its four columns; g, beta)
-    struct In {
-        float qv[QK], kv[QK], vv[4], gg, bb;
+    // A step's q and k (this thread's share, for the LDS copy), fetched two
+    // steps ahead since they go to LDS one step ahead; its v (this thread's
+    // four columns), g and beta, fetched one step ahead.
+    struct QkIn {
+        float qv[QK], kv[QK];
     };
-    auto fetch = [&](In &in, int t) {
+    struct VIn {
+        float vv[4], gg, bb;
+    };
+    auto fetch_qk = [&](QkIn &in, int t) {
         const int64_t tt = t < nsteps ? t : nsteps - 1;
 #pragma unroll
         for (int e = 0; e < QK; ++e) {
@@ -234,28 +239,44 @@ void gdn_steps_kernel(
             in.qv[e] = idx < DK ? gdn_f<T>(qb[tt * qks + idx]) : 0.f;
             in.kv[e] = idx < DK ? gdn_f<T>(kb[tt * qks + idx]) : 0.f;
         }
+    };
+    auto fetch_v = [&](VIn &in, int t) {
+        const int64_t tt = t < nsteps ? t : nsteps - 1;
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             in.vv[e] = gdn_f<T>(vb[tt * vs + e]);
         in.gg = g[tt * gs + bj];
         in.bb = beta[tt * gs + bj];
     };
-
-    In cur, nxt;
-    fetch(cur, 0);
-    float sc = 1.f;
-    for (int t = 0; t < nsteps; ++t) {
-        const int pb = t & 1;
+    auto put_qk = [&](const QkIn &in, int buf) {
 #pragma unroll
         for (int e = 0; e < QK; ++e) {
             const int idx = tid + e * kGdnThreads;
             if (idx < DK) {
-                sq[pb][idx] = cur.qv[e];
-                sk[pb][idx] = cur.kv[e];
+                sq[buf][idx] = in.qv[e];
+                sk[buf][idx] = in.kv[e];
             }
         }
-        fetch(nxt, t + 1);
-        __syncthreads();   // q, k of step t in LDS; last step's partials consumed
+    };
+
+    QkIn qkn;
+    VIn cur, nxt;
+    fetch_qk(qkn, 0);
+    put_qk(qkn, 0);
+    fetch_qk(qkn, 1);
+    fetch_v(cur, 0);
+    __syncthreads();   // step 0's q, k in LDS
+    float sc = 1.f;
+    for (int t = 0; t < nsteps; ++t) {
+        const int pb = t % 3, nb = pb == 2 ? 0 : pb + 1, hb = t & 1;
+        // Step t + 1's q and k go to the next buffer now; they are read after
+        // this step's barrier.  That buffer was last read in step t - 2, which
+        // every thread finished before it reached step t - 1's barrier, and
+        // part[hb] / sqk[hb] were last read in step t - 2 the same way, so one
+        // barrier per step suffices.
+        put_qk(qkn, nb);
+        fetch_qk(qkn, t + 2);
+        fetch_v(nxt, t + 1);
         float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), pp = pr;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -276,9 +297,9 @@ void gdn_steps_kernel(
         wave_sum(pr);
         wave_sum(pp);
         if (lg == 0)
-            part[w][lc][0] = pr;
+            part[hb][w][lc][0] = pr;
         else if (lg == 1)
-            part[w][lc][1] = pp;
+            part[hb][w][lc][1] = pp;
         if (w == 1) {   // q . k (wave 1, so wave 0 is free for the delta below)
             float d = 0.f;
 #pragma unroll
@@ -288,13 +309,13 @@ void gdn_steps_kernel(
             for (int off = 32; off > 0; off >>= 1)
                 d += __shfl_xor(d, off, 64);
             if (lane == 0)
-                sqk = d;
+                sqk[hb] = d;
         }
-        __syncthreads();   // partials and q . k in LDS
-        float4 R = part[0][lc][0], Pq = part[0][lc][1];
+        __syncthreads();   // partials, q . k and step t + 1's q, k in LDS
+        float4 R = part[hb][0][lc][0], Pq = part[hb][0][lc][1];
 #pragma unroll
         for (int m = 1; m < 4; ++m) {
-            const float4 a = part[m][lc][0], c = part[m][lc][1];
+            const float4 a = part[hb][m][lc][0], c = part[hb][m][lc][1];
             R.x += a.x; R.y += a.y; R.z += a.z; R.w += a.w;
             Pq.x += c.x; Pq.y += c.y; Pq.z += c.z; Pq.w += c.w;
         }
@@ -307,7 +328,7 @@ void gdn_steps_kernel(
         d.w = cur.bb * (cur.vv[3] - cur.gg * R.w);
         if (tid < LPR) {
             T *oj = ob + (int64_t)t * vs;
-            const float qk = sqk;
+            const float qk = sqk[hb];
             oj[0] = gdn_t<T>(cur.gg * Pq.x + qk * d.x);
             oj[1] = gdn_t<T>(cur.gg * Pq.y + qk * d.y);
             oj[2] = gdn_t<T>(cur.gg * Pq.z + qk * d.z);
