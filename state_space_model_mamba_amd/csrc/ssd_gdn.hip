@@ -183,9 +183,10 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
 // hardware reciprocal (within 1 ulp).
 // q, k [S, B, Hk, DK], v, o [S, B, Hv, dv], g, beta [S, B, Hv].
 // Occupancy: a thread holds DK * CT / 256 state elements.  At 64 (dk = dv =
-// 128) the kernel is held to four waves per SIMD (128 VGPRs; the compiler
-// alone took 160 and three waves, 18% slower at batch 256 with no spill inside
-// the step loop); larger slices are left to the compiler.
+// 128, or dk = 256 on 64-column tiles) the kernel is held to four waves per
+// SIMD (128 VGPRs, no spill inside the step loop; the compiler alone took 160
+// and three waves, 18% slower at batch 256); smaller slices need fewer
+// registers anyway.
 template <typename T, int DK, int CT>
 __global__ __launch_bounds__(kGdnThreads) __attribute__((amdgpu_waves_per_eu(DK * CT <= 128 * 128 ? 4 : 1)))
 void gdn_steps_kernel(
@@ -375,12 +376,17 @@ hipError_t gdn_steps_dispatch_dv(int64_t S, int64_t B, int64_t Hk, int64_t Hv, i
             *vv = static_cast<const T *>(v);
     T *oo = static_cast<T *>(o);
     const int n = (int)S, b = (int)B, hk = (int)Hk, hv = (int)Hv, d = (int)dv;
-    if (ct == 64)
+    if constexpr (DK == 256) {
         gdn_steps_kernel<T, DK, 64><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv, g,
                                                                  beta, state, oo);
-    else
-        gdn_steps_kernel<T, DK, 128><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv, g,
-                                                                  beta, state, oo);
+    } else {
+        if (ct == 64)
+            gdn_steps_kernel<T, DK, 64><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv,
+                                                                     g, beta, state, oo);
+        else
+            gdn_steps_kernel<T, DK, 128><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk,
+                                                                      vv, g, beta, state, oo);
+    }
     return hipGetLastError();
 }
 
