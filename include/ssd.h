@@ -192,8 +192,11 @@ ssd_status ssd_decode_step(const ssd_dims *dims, const void *x, const float *dt,
 
 /*
  * ssd_decode_steps -- nsteps consecutive cached decode steps in one launch:
- * the same result as calling ssd_decode_step nsteps times, step k on the k-th
- * slice of each input, but the state is read once, kept on-chip (in
+ * the result of calling ssd_decode_step nsteps times, step k on the k-th
+ * slice of each input, up to rounding (between steps the state may be held
+ * divided by the product of the decays since its last rescale, which rounds
+ * differently; both forms meet the same tolerance against the exact
+ * recurrence), but the state is read once, kept on-chip (in
  * registers) across all steps and written once (section 2 of the page: the
  * decode loop runs on the device around the state cache; "A Persistent-State
  * Dataflow Accelerator for Memory-Bound Linear Attention Decode on FPGA",
@@ -249,8 +252,10 @@ ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const vo
 
 /*
  * ssd_gdn_decode_steps -- nsteps Gated DeltaNet decode steps in one launch:
- * the same result as nsteps ssd_gdn_decode_step calls on consecutive slices,
- * with the state read once, kept on-chip (in registers) across the steps and
+ * the result of nsteps ssd_gdn_decode_step calls on consecutive slices, up
+ * to rounding (between steps the state is held divided by the product of the
+ * gates since its last rescale), with the state read once, kept on-chip (in
+ * registers) across the steps and
  * written once (section 2A of the FPGA page: a state persistent on-chip is not
  * re-read from external memory between steps).
  *   q, k [S, B, Hk, dk]; v, o [S, B, Hv, dv]; g, beta [S, B, Hv]; S = nsteps
