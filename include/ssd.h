@@ -255,9 +255,9 @@ ssd_status ssd_gdn_decode_step(const ssd_gdn_dims *dims, const void *q, const vo
  * the result of nsteps ssd_gdn_decode_step calls on consecutive slices, up
  * to rounding (between steps the state is held divided by the product of the
  * gates since its last rescale), with the state read once, kept on-chip (in
- * registers) across the steps and
- * written once (section 2A of the FPGA page: a state persistent on-chip is not
- * re-read from external memory between steps).
+ * registers) across the steps and written once (section 2A of the FPGA page:
+ * a state persistent on-chip is not re-read from external memory between
+ * steps).
  *   q, k [S, B, Hk, dk]; v, o [S, B, Hv, dv]; g, beta [S, B, Hv]; S = nsteps
  *   state [B, Hv, dk, dv] fp32, updated in place
  * nsteps == 0 or B == 0 does nothing; nsteps < 0 is SSD_ERR_SHAPE.  Shapes,
