@@ -154,3 +154,17 @@ def test_gdn_steps_gate_extremes(io):
     o, s = run_steps_launch(tok, io)
     oref, sref = oracle_run(tok, io)
     check(o, s, oref, sref, TOL[io], f"gdn steps gate extremes {io}")
+
+
+@pytest.mark.parametrize("steps", [1, 2, 3, 4])
+@pytest.mark.parametrize("dk,dv,Hk,Hv", [(128, 128, 2, 4), (256, 64, 1, 1)])
+def test_gdn_steps_few_steps(steps, dk, dv, Hk, Hv):
+    """Launches of 1 to 4 steps: the start of the launch's pipeline (q and k
+    two steps ahead through three LDS buffers, clamped fetches past the last
+    step) against the oracle and single-step calls."""
+    tok = si.gdn_tokens(900 + steps + dk, steps, 3, Hk, Hv, dk, dv, "bf16")
+    o, s = run_steps_launch(tok, "bf16")
+    oref, sref = oracle_run(tok, "bf16")
+    check(o, s, oref, sref, TOL["bf16"], f"gdn {steps} steps dk={dk} dv={dv}")
+    o1, s1 = run(tok, "bf16", steps)
+    check(o, s, o1.astype(np.float64), s1.astype(np.float64), TOL["bf16"], f"gdn {steps} steps vs single")
