@@ -250,16 +250,170 @@ struct RunRef {
 
 std::vector<std::vector<RunRef>> bf16_groups(const ssd_dims *d, const int64_t *cu);
 
+// Segment counts for the runs of one launch (two or more runs).  Both kernels
+// run one work-group per CU, and the hardware starts work-groups in index
+// order, the runs being laid out longest segments first.  Modelled time of a
+// choice: the state kernel's 64-token tile-quads (the tiles of every segment
+// but a run's last, times its sequences and head quads) spread over the chip,
+// plus the longest-first list schedule of the scan kernel's work-groups on 256
+// CUs, each as long as its segment's tiles plus about one tile per unit state
+// it chains -- so that short work-groups may run in a second round on CUs
+// that free up early.  Costs per tile as measured at the 2.7B layer: ~2.8 us
+// per tile-quad and CU (state kernel), ~4.85 us per tile (scan kernel).  The
+// candidates share a longest segment length T: each run takes the fewest
+// segments of at most T chunks, for T = ceil(nchunks / k) of the longest run,
+// k = 1 .. 64.
+constexpr int64_t kCUsModel = 256;
+constexpr double kStateTileUs = 2.8, kScanTileUs = 4.85;
+
+int64_t run_cus(const RunRef &r, int64_t total)
+{
+    return std::max<int64_t>(8, (256 * r.B * r.L + total - 1) / std::max<int64_t>(total, 1));
+}
+
+// A run's segment shape for a segment count, memoised per run.
+struct SegShape {
+    int64_t nseg, seg_tok, last_tok, nsub;
+};
+
+struct GroupModel {
+    const ssd_dims *d;
+    const std::vector<RunRef> &grp;
+    int64_t total;
+    std::vector<std::vector<std::pair<int64_t, SegShape>>> memo;
+    std::vector<std::pair<double, int64_t>> jobs, load, next, raised;   // reused buffers
+
+    GroupModel(const ssd_dims *dd, const std::vector<RunRef> &g, int64_t t)
+        : d(dd), grp(g), total(t), memo(g.size()) {}
+
+    SegShape shape(size_t r, int64_t nseg)
+    {
+        for (const auto &m : memo[r])
+            if (m.first == nseg)
+                return m.second;
+        const ssd::Bf16Plan p = ssd::plan_scan_bf16(grp[r].B, grp[r].L, d->nheads, d->ngroups,
+                                                    d->chunk, run_cus(grp[r], total), nseg, false);
+        const int64_t seg_tok = p.chunks_per_seg * d->chunk;
+        const SegShape sh{p.nseg, seg_tok, grp[r].L - (p.nseg - 1) * seg_tok, p.nsub};
+        memo[r].push_back({nseg, sh});
+        return sh;
+    }
+
+    double cost(const std::vector<int64_t> &nseg)
+    {
+        const int64_t hg = d->nheads / d->ngroups, quads = d->ngroups * ((hg + 3) / 4);
+        double state_tiles = 0.0;
+        jobs.clear();   // (tiles, work-groups)
+        for (size_t r = 0; r < grp.size(); ++r) {
+            const SegShape sh = shape(r, nseg[r]);
+            const int64_t wgs = grp[r].B * quads;
+            state_tiles += (double)wgs * (double)(grp[r].L - sh.last_tok) / 64.0;
+            for (int64_t sg = 0; sg < sh.nseg; ++sg) {
+                const int64_t tok = sg + 1 < sh.nseg ? sh.seg_tok : sh.last_tok;
+                jobs.push_back({std::max(1.0, (double)tok / 64.0) + (double)(sg * sh.nsub), wgs});
+            }
+        }
+        std::sort(jobs.begin(), jobs.end(), [](const auto &x, const auto &y) { return x.first > y.first; });
+        // CU loads as (load, CUs) buckets in ascending load; each job goes to
+        // a least-loaded CU
+        load.assign(1, {0.0, kCUsModel});
+        for (const auto &j : jobs) {
+            const int64_t full = j.second / kCUsModel;
+            int64_t rem = j.second % kCUsModel;
+            next.clear();
+            raised.clear();
+            for (auto &bk : load) {
+                bk.first += (double)full * j.first;
+                const int64_t take = std::min(rem, bk.second);
+                rem -= take;
+                if (take > 0)
+                    raised.push_back({bk.first + j.first, take});
+                if (bk.second > take)
+                    next.push_back({bk.first, bk.second - take});
+            }
+            // merge the two ascending lists back into load, joining equal loads
+            load.clear();
+            size_t a = 0, b = 0;
+            while (a < next.size() || b < raised.size()) {
+                const bool from_next = b == raised.size() || (a < next.size() && next[a].first < raised[b].first);
+                const std::pair<double, int64_t> bk = from_next ? next[a++] : raised[b++];
+                if (!load.empty() && load.back().first == bk.first)
+                    load.back().second += bk.second;
+                else
+                    load.push_back(bk);
+            }
+        }
+        return kStateTileUs * state_tiles / (double)kCUsModel + kScanTileUs * load.back().first;
+    }
+};
+
+std::vector<int64_t> group_nseg_search(const ssd_dims *d, const std::vector<RunRef> &grp,
+                                       int64_t total)
+{
+    const int64_t Q = d->chunk;
+    int64_t maxch = 1;
+    for (const RunRef &r : grp)
+        maxch = std::max(maxch, (r.L + Q - 1) / Q);
+    GroupModel model(d, grp, total);
+    std::vector<int64_t> best;
+    double best_cost = 0.0;
+    int64_t last_T = -1;
+    for (int64_t k = 1; k <= std::min<int64_t>(maxch, 64); ++k) {
+        const int64_t T = (maxch + k - 1) / k;           // longest segment, chunks
+        if (T == last_T)
+            continue;
+        last_T = T;
+        std::vector<int64_t> nseg(grp.size());
+        for (size_t r = 0; r < grp.size(); ++r)
+            nseg[r] = ((grp[r].L + Q - 1) / Q + T - 1) / T;
+        const double c = model.cost(nseg);
+        if (best.empty() || c < best_cost) {
+            best = nseg;
+            best_cost = c;
+        }
+    }
+    return best;
+}
+
+// The search above takes ~20 us for eight runs; an entry point plans the same
+// group several times (workspace query, validation, launch), and serving
+// loops repeat batch shapes, so the last few answers are kept per thread.
+std::vector<int64_t> group_nseg(const ssd_dims *d, const std::vector<RunRef> &grp, int64_t total)
+{
+    struct Entry {
+        std::vector<int64_t> key, nseg;
+    };
+    thread_local std::vector<Entry> cache;
+    std::vector<int64_t> key{d->nheads, d->ngroups, d->chunk};
+    for (const RunRef &r : grp) {
+        key.push_back(r.B);
+        key.push_back(r.L);
+    }
+    for (const Entry &e : cache)
+        if (e.key == key)
+            return e.nseg;
+    std::vector<int64_t> nseg = group_nseg_search(d, grp, total);
+    if (cache.size() == 8)
+        cache.erase(cache.begin());
+    cache.push_back(Entry{key, nseg});
+    return nseg;
+}
+
 size_t group_plans(const ssd_dims *d, const std::vector<RunRef> &grp,
                    std::vector<ssd::Bf16Plan> *plans)
 {
     int64_t total = 0;
     for (const RunRef &r : grp)
         total += r.B * r.L;
+    // one run: the planner of the batched scan (a packed batch of equal
+    // lengths is then the batched scan, bit for bit)
+    const std::vector<int64_t> nseg = grp.size() > 1 ? group_nseg(d, grp, total)
+                                                     : std::vector<int64_t>(grp.size(), 0);
     size_t bytes = 0;
-    for (const RunRef &r : grp) {
-        const int64_t cus = std::max<int64_t>(8, (256 * r.B * r.L + total - 1) / std::max<int64_t>(total, 1));
-        const ssd::Bf16Plan p = ssd::plan_scan_bf16(r.B, r.L, d->nheads, d->ngroups, d->chunk, cus);
+    for (size_t i = 0; i < grp.size(); ++i) {
+        const RunRef &r = grp[i];
+        const ssd::Bf16Plan p = ssd::plan_scan_bf16(r.B, r.L, d->nheads, d->ngroups, d->chunk,
+                                                    run_cus(r, total), nseg[i]);
         if (plans)
             plans->push_back(p);
         bytes += (p.ws_bytes + 255) / 256 * 256;
@@ -581,11 +735,20 @@ SSD_EXPORT ssd_status ssd_chunk_scan_varlen(const ssd_dims *dims, const int64_t 
     for (const auto &grp : groups) {
         std::vector<ssd::Bf16Plan> plans;
         group_plans(dims, grp, &plans);
+        // runs with the longest segments first: the hardware starts their
+        // work-groups first, and short ones fill the CUs that free up
+        std::vector<size_t> order(grp.size());
+        for (size_t r = 0; r < order.size(); ++r)
+            order[r] = r;
+        std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
+            return plans[a].chunks_per_seg * dims->chunk > plans[b].chunks_per_seg * dims->chunk;
+        });
         ssd::Bf16Run runs[ssd::kMaxRuns];
         char *wsp = static_cast<char *>(workspace);
-        for (size_t r = 0; r < grp.size(); ++r) {
+        for (size_t i = 0; i < grp.size(); ++i) {
+            const size_t r = order[i];
             const RunRef &u = grp[r];
-            runs[r] = ssd::Bf16Run{plans[r], u.B, u.L, xb + u.tok * H * P * esz, dt + u.tok * H,
+            runs[i] = ssd::Bf16Run{plans[r], u.B, u.L, xb + u.tok * H * P * esz, dt + u.tok * H,
                                    bb + u.tok * G * N * esz, cb + u.tok * G * N * esz,
                                    initial_states ? initial_states + u.seq * HPN : nullptr,
                                    yb + u.tok * H * P * esz, final_states + u.seq * HPN, wsp};

@@ -112,8 +112,11 @@ struct Bf16Plan {
     size_t decay_bytes;    // B*H*nslot*4
     size_t ws_bytes;       // total workspace
 };
-// cus: the CUs the problem may count on (fewer when it shares a launch).
-Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, int64_t cus = 256);
+// cus: the CUs the problem may count on (fewer when it shares a launch);
+// nseg > 0 fixes the segment count.  With use_env the SSD_NSEG / SSD_NSUB
+// environment variables, when set, override the segment and unit counts.
+Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, int64_t cus = 256,
+                        int64_t nseg = 0, bool use_env = true);
 
 hipError_t launch_scan_bf16(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t G,
                             int64_t Q, const void *x, const float *dt, const float *A,

@@ -1129,7 +1129,8 @@ static size_t align256(size_t n)
     return (n + 255) / 256 * 256;
 }
 
-Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, int64_t cus)
+Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, int64_t cus,
+                        int64_t nseg_fixed, bool use_env)
 {
     const int64_t kCUs = std::max<int64_t>(1, cus);
     Bf16Plan p{};
@@ -1144,7 +1145,9 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, i
     // time is ~ rounds * chunks per segment; the state kernel (about half the
     // work per tile) re-reads x for all but the last segment, and every segment
     // adds state traffic through the workspace.
-    int64_t nseg = env_int("SSD_NSEG", 0);
+    int64_t nseg = use_env ? env_int("SSD_NSEG", 0) : 0;
+    if (nseg <= 0)
+        nseg = nseg_fixed;
     if (nseg <= 0) {
         double best = 1e300;
         for (int64_t k = 1; k <= std::max<int64_t>(p.nchunks, 1); ++k) {
@@ -1172,7 +1175,7 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, i
     p.nsub = 1;
     p.unit_tokens = p.chunks_per_seg * Q;
     if (p.nseg > 1) {
-        int64_t want = env_int("SSD_NSUB", 0);
+        int64_t want = use_env ? env_int("SSD_NSUB", 0) : 0;
         double best = 1e300;
         for (int64_t k = 1; k <= 8; ++k) {
             const int64_t ut = (seg_tiles + k - 1) / k;             // tiles per unit
