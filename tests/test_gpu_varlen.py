@@ -97,3 +97,16 @@ def test_varlen_2p7b_heads():
     w, inp, A, D = packed(int(cu[-1]), 80, 1, seed=104, chunk=256)
     y, fs = run_varlen(inp, A, D, cu, 256)
     check_sequences(inp, A, D, cu, y, fs, None, [0, 41, 79], "varlen 2.7B")
+
+
+def test_varlen_more_runs_than_one_launch():
+    """Ten runs of distinct lengths (two launch groups of at most eight runs),
+    from a 1-token sequence to 3000 tokens, with segment counts from the group
+    planner; sampled heads of every sequence against the oracle."""
+    lengths = [3000, 1, 130, 2500, 640, 1999, 64, 900, 1200, 257]
+    cu = np.concatenate([[0], np.cumsum(lengths)]).astype(np.int64)
+    H = 12
+    w, inp, A, D = packed(int(cu[-1]), H, 3, seed=105, chunk=128)
+    init0 = np.random.default_rng(9).standard_normal((len(lengths), H, 64, 128)).astype(np.float32)
+    y, fs = run_varlen(inp, A, D, cu, 128, init=dev(init0))
+    check_sequences(inp, A, D, cu, y, fs, init0, [0, 5, 11], "varlen 10 runs")
