@@ -73,7 +73,6 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
     constexpr int RPI = 64 / LPR;           // rows covered by one load instruction of a wave
     constexpr int ROWS = DK / (4 * RPI);    // rows per lane
     static_assert(ROWS >= 1 && ROWS * 4 * RPI == DK, "DK rows split over 4 waves x RPI");
-    __shared__ float sk[DK], sq[DK];
     __shared__ float4 part[4 * RPI][LPR][2];   // per (wave, lane group): r and p of 4 columns
     __shared__ float4 sdv[LPR];
     __shared__ float sqk;
@@ -87,11 +86,16 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
     const int c0 = tile * CT + 4 * lc;                  // first of the lane's 4 columns
     const int r0 = (w * RPI + lg) * ROWS;               // first of the lane's ROWS rows
 
-    // q and k of the query/key head, widened once into LDS
+    // q and k of the lane's rows, widened into registers straight from memory
+    // (not through LDS: no barrier before the first pass, so a wave starts as
+    // soon as its own state loads land; 3% faster at batch 256, although the
+    // kernel then runs two waves per SIMD instead of three)
     const T *qi = q + ((int64_t)b * Hk + i) * DK, *ki = k + ((int64_t)b * Hk + i) * DK;
-    for (int e = tid; e < DK; e += kGdnThreads) {
-        sk[e] = gdn_f<T>(ki[e]);
-        sq[e] = gdn_f<T>(qi[e]);
+    float kr_[ROWS], qr_[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+        kr_[r] = gdn_f<T>(ki[r0 + r]);
+        qr_[r] = gdn_f<T>(qi[r0 + r]);
     }
     float *S = state + ((int64_t)bj * DK + r0) * dv + c0;
     float4 s[ROWS];
@@ -99,13 +103,12 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
     for (int r = 0; r < ROWS; ++r)
         s[r] = gdn_ld<kNT>(S + (int64_t)r * dv);
     const float gj = g[bj], bt = beta[bj];
-    __syncthreads();
 
     // pass 1 (read): partial retrieval r = S^T k and readout p = S^T q
     float4 pr = make_float4(0.f, 0.f, 0.f, 0.f), pp = pr;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-        const float kr = sk[r0 + r], qr = sq[r0 + r];
+        const float kr = kr_[r], qr = qr_[r];
         pr.x += kr * s[r].x; pr.y += kr * s[r].y; pr.z += kr * s[r].z; pr.w += kr * s[r].w;
         pp.x += qr * s[r].x; pp.y += qr * s[r].y; pp.z += qr * s[r].z; pp.w += qr * s[r].w;
     }
@@ -115,7 +118,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
         float d = 0.f;
 #pragma unroll
         for (int e = lane; e < DK; e += 64)
-            d += sq[e] * sk[e];
+            d += gdn_f<T>(qi[e]) * gdn_f<T>(ki[e]);
 #pragma unroll
         for (int off = 32; off > 0; off >>= 1)
             d += __shfl_xor(d, off, 64);
@@ -152,7 +155,7 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
     const float4 d = sdv[lc];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-        const float kr = sk[r0 + r];
+        const float kr = kr_[r];
         float4 n;
         n.x = gj * s[r].x + kr * d.x;
         n.y = gj * s[r].y + kr * d.y;
