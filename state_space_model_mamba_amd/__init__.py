@@ -129,6 +129,46 @@ def _io_dtype(t):
     raise TypeError(f"x/B/C must be bfloat16 or float32, got {t.dtype}")
 
 
+def _need(name, t, dev, dtype=None, shape=None, optional=False):
+    """Checks that a tensor argument can be handed to the kernels as a plain
+    device pointer: a contiguous tensor on `dev` of the stated dtype and shape.
+    A host tensor would hand a host address to a kernel, and a strided view or a
+    wrong dtype would be read as something else, so each raises here instead."""
+    import torch
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.device != dev:
+        raise ValueError(f"{name} is on {t.device}, expected {dev}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _device_of(t):
+    """The device of the first tensor argument, which must be a GPU tensor."""
+    if t.device.type != "cuda":
+        raise ValueError(f"arguments must be device (HIP) tensors, got one on {t.device}")
+    return t.device
+
+
+def _stream_obj(stream, dev):
+    import torch
+    return torch.cuda.current_stream(dev) if stream is None else stream
+
+
+def _bias_check(dev, H, dt_softplus, dt_bias):
+    import torch
+    if dt_softplus:
+        _need("dt_bias", dt_bias, dev, torch.float32, (H,), optional=True)
+
+
 def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype,
               dt_softplus=False, dt_bias=None) -> SsdDims:
     """ssd_dims; with dt_softplus the dt arguments hold u and the step size is
@@ -149,7 +189,13 @@ def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroup
 
 def ssd_state_init(state, src=None, stream=None):
     """state [B, H, P, N] fp32 <- src (or zeros)."""
+    import torch
+    dev = _device_of(state)
+    _need("state", state, dev, torch.float32)
+    if state.dim() != 4:
+        raise ValueError(f"state must be [B, H, P, N], got shape {tuple(state.shape)}")
     b, h, p, n = state.shape
+    _need("src", src, dev, torch.float32, state.shape, optional=True)
     d = make_dims(b, 0, h, p, n, 1, 1, SSD_F32)
     _check("ssd_state_init", load().ssd_state_init(ctypes.byref(d), _ptr(state), _ptr(src),
                                                    _stream(stream)))
@@ -157,30 +203,48 @@ def ssd_state_init(state, src=None, stream=None):
 
 
 def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
-               dt_softplus=False, dt_bias=None):
+               dt_softplus=False, dt_bias=None, stream=None):
     import torch
+    dev = _device_of(x)
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [B, L, H, P] and B, C [B, L, G, N]")
     bsz, L, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
     io = _io_dtype(x)
+    f32 = torch.float32
+    _need("x", x, dev, x.dtype)
+    _need("dt", dt, dev, f32, (bsz, L, H))
+    _need("A", A, dev, f32, (H,))
+    _need("B", B, dev, x.dtype, (bsz, L, G, N))
+    _need("C", C, dev, x.dtype, (bsz, L, G, N))
+    _need("D", D, dev, f32, (H,))
+    _need("initial_state", initial_state, dev, f32, (bsz, H, P, N), optional=True)
+    _need("y", y, dev, x.dtype, x.shape, optional=True)
+    _need("final_state", final_state, dev, f32, (bsz, H, P, N), optional=True)
+    _need("workspace", workspace, dev, optional=True)
+    _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(bsz, L, H, P, N, G, chunk, io, dt_softplus, dt_bias)
-    if y is None:
-        y = torch.empty_like(x)
-    if final_state is None:
-        final_state = torch.empty((bsz, H, P, N), dtype=torch.float32, device=x.device)
     need = ssd_chunk_scan_workspace_size(bsz, L, H, P, N, G, chunk, io)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    # outputs and workspace come from the allocator on the call's own stream, so
+    # that their blocks are not handed to other work while the kernels run
+    with torch.cuda.stream(_stream_obj(stream, dev)):
+        if y is None:
+            y = torch.empty_like(x)
+        if final_state is None:
+            final_state = torch.empty((bsz, H, P, N), dtype=f32, device=dev)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     args = [ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
             _ptr(initial_state), _ptr(y), _ptr(final_state), _ptr(workspace), ws_bytes]
-    return args, y, final_state
+    return args, y, final_state, workspace
 
 
 def ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_state=None,
                    workspace=None, stream=None, dt_softplus=False, dt_bias=None):
     """Prefill over x[B, L, H, P]; returns (y, final_state)."""
-    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
-                             dt_softplus, dt_bias)
+    args, y, fs, ws = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state,
+                                 workspace, dt_softplus, dt_bias, stream)
     _check("ssd_chunk_scan", load().ssd_chunk_scan(*args, _stream(stream)))
     return y, fs
 
@@ -188,8 +252,8 @@ def ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_s
 def ssd_chunk_scan_timed(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_state=None,
                          workspace=None, stream=None, dt_softplus=False, dt_bias=None):
     """As ssd_chunk_scan, synchronously, also returning [(kernel name, ms), ...]."""
-    args, y, fs = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
-                             dt_softplus, dt_bias)
+    args, y, fs, ws = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state,
+                                 workspace, dt_softplus, dt_bias, stream)
     cap = 8
     ms = (ctypes.c_float * cap)()
     names = (ctypes.c_char_p * cap)()
@@ -203,11 +267,25 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=F
                     dt_bias=None):
     """One decode step: x[B, H, P], B/C[B, G, N], state[B, H, P, N] updated in place; returns y."""
     import torch
+    dev = _device_of(x)
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [B, H, P] and B, C [B, G, N]")
     bsz, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
+    f32 = torch.float32
+    _need("x", x, dev, x.dtype)
+    _need("dt", dt, dev, f32, (bsz, H))
+    _need("A", A, dev, f32, (H,))
+    _need("B", B, dev, x.dtype, (bsz, G, N))
+    _need("C", C, dev, x.dtype, (bsz, G, N))
+    _need("D", D, dev, f32, (H,))
+    _need("state", state, dev, f32, (bsz, H, P, N))
+    _need("y", y, dev, x.dtype, x.shape, optional=True)
+    _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x), dt_softplus, dt_bias)
     if y is None:
-        y = torch.empty_like(x)
+        with torch.cuda.stream(_stream_obj(stream, dev)):
+            y = torch.empty_like(x)
     _check("ssd_decode_step", load().ssd_decode_step(
         ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
         _ptr(y), _stream(stream)))
@@ -219,11 +297,25 @@ def ssd_decode_steps(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=
     """S decode steps in one launch: x[S, B, H, P], dt[S, B, H], B/C[S, B, G, N];
     state[B, H, P, N] updated in place (read and written once); returns y[S, B, H, P]."""
     import torch
+    dev = _device_of(x)
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [S, B, H, P] and B, C [S, B, G, N]")
     nsteps, bsz, H, P = x.shape
     G, N = B.shape[2], B.shape[3]
+    f32 = torch.float32
+    _need("x", x, dev, x.dtype)
+    _need("dt", dt, dev, f32, (nsteps, bsz, H))
+    _need("A", A, dev, f32, (H,))
+    _need("B", B, dev, x.dtype, (nsteps, bsz, G, N))
+    _need("C", C, dev, x.dtype, (nsteps, bsz, G, N))
+    _need("D", D, dev, f32, (H,))
+    _need("state", state, dev, f32, (bsz, H, P, N))
+    _need("y", y, dev, x.dtype, x.shape, optional=True)
+    _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x), dt_softplus, dt_bias)
     if y is None:
-        y = torch.empty_like(x)
+        with torch.cuda.stream(_stream_obj(stream, dev)):
+            y = torch.empty_like(x)
     _check("ssd_decode_steps", load().ssd_decode_steps(
         ctypes.byref(d), ctypes.c_int64(nsteps), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
         _ptr(D), _ptr(state), _ptr(y), _stream(stream)))
@@ -253,19 +345,35 @@ def ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, initial_states=N
     tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (a host sequence of S + 1 offsets).
     Returns (y[T, H, P], final_states[S, H, P, N])."""
     import torch
+    dev = _device_of(x)
+    if x.dim() != 3 or B.dim() != 3:
+        raise ValueError("x must be [T, H, P] and B, C [T, G, N]")
     T, H, P = x.shape
     G, N = B.shape[1], B.shape[2]
     cu, cup = _cu_array(cu_seqlens)
     nseq = len(cu) - 1
     io = _io_dtype(x)
+    f32 = torch.float32
+    _need("x", x, dev, x.dtype)
+    _need("dt", dt, dev, f32, (T, H))
+    _need("A", A, dev, f32, (H,))
+    _need("B", B, dev, x.dtype, (T, G, N))
+    _need("C", C, dev, x.dtype, (T, G, N))
+    _need("D", D, dev, f32, (H,))
+    _need("initial_states", initial_states, dev, f32, (nseq, H, P, N), optional=True)
+    _need("y", y, dev, x.dtype, x.shape, optional=True)
+    _need("final_states", final_states, dev, f32, (nseq, H, P, N), optional=True)
+    _need("workspace", workspace, dev, optional=True)
+    _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(nseq, T, H, P, N, G, chunk, io, dt_softplus, dt_bias)
-    if y is None:
-        y = torch.empty_like(x)
-    if final_states is None:
-        final_states = torch.empty((nseq, H, P, N), dtype=torch.float32, device=x.device)
     need = ssd_chunk_scan_varlen_workspace_size(cu, H, P, N, G, chunk, io)
-    if workspace is None and need > 0:
-        workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    with torch.cuda.stream(_stream_obj(stream, dev)):
+        if y is None:
+            y = torch.empty_like(x)
+        if final_states is None:
+            final_states = torch.empty((nseq, H, P, N), dtype=f32, device=dev)
+        if workspace is None and need > 0:
+            workspace = torch.empty(need, dtype=torch.uint8, device=dev)
     ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
     _check("ssd_chunk_scan_varlen", load().ssd_chunk_scan_varlen(
         ctypes.byref(d), cup, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
@@ -278,11 +386,23 @@ def ssd_gdn_decode_step(q, k, v, g, beta, state, o=None, stream=None):
     """One Gated DeltaNet decode step: q, k [B, Hk, dk], v [B, Hv, dv], g, beta [B, Hv]
     fp32, state [B, Hv, dk, dv] fp32 updated in place; returns o [B, Hv, dv]."""
     import torch
+    dev = _device_of(q)
+    if q.dim() != 3 or v.dim() != 3:
+        raise ValueError("q, k must be [B, Hk, dk] and v [B, Hv, dv]")
     bsz, Hk, dk = q.shape
     Hv, dv = v.shape[1], v.shape[2]
+    f32 = torch.float32
+    _need("q", q, dev, q.dtype)
+    _need("k", k, dev, q.dtype, q.shape)
+    _need("v", v, dev, q.dtype)
+    _need("g", g, dev, f32, (bsz, Hv))
+    _need("beta", beta, dev, f32, (bsz, Hv))
+    _need("state", state, dev, f32, (bsz, Hv, dk, dv))
+    _need("o", o, dev, q.dtype, v.shape, optional=True)
     d = SsdGdnDims(bsz, Hk, Hv, dk, dv, _io_dtype(q), 0)
     if o is None:
-        o = torch.empty_like(v)
+        with torch.cuda.stream(_stream_obj(stream, dev)):
+            o = torch.empty_like(v)
     _check("ssd_gdn_decode_step", load().ssd_gdn_decode_step(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
         _stream(stream)))
@@ -293,11 +413,23 @@ def ssd_gdn_decode_steps(q, k, v, g, beta, state, o=None, stream=None):
     """S Gated DeltaNet steps in one launch: q, k [S, B, Hk, dk], v [S, B, Hv, dv],
     g, beta [S, B, Hv]; state [B, Hv, dk, dv] read and written once; returns o [S, B, Hv, dv]."""
     import torch
+    dev = _device_of(q)
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q, k must be [S, B, Hk, dk] and v [S, B, Hv, dv]")
     nsteps, bsz, Hk, dk = q.shape
     Hv, dv = v.shape[2], v.shape[3]
+    f32 = torch.float32
+    _need("q", q, dev, q.dtype)
+    _need("k", k, dev, q.dtype, q.shape)
+    _need("v", v, dev, q.dtype)
+    _need("g", g, dev, f32, (nsteps, bsz, Hv))
+    _need("beta", beta, dev, f32, (nsteps, bsz, Hv))
+    _need("state", state, dev, f32, (bsz, Hv, dk, dv))
+    _need("o", o, dev, q.dtype, v.shape, optional=True)
     d = SsdGdnDims(bsz, Hk, Hv, dk, dv, _io_dtype(q), 0)
     if o is None:
-        o = torch.empty_like(v)
+        with torch.cuda.stream(_stream_obj(stream, dev)):
+            o = torch.empty_like(v)
     _check("ssd_gdn_decode_steps", load().ssd_gdn_decode_steps(
         ctypes.byref(d), ctypes.c_int64(nsteps), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(state), _ptr(o), _stream(stream)))

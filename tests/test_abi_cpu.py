@@ -281,3 +281,20 @@ def test_gdn_steps_validation(lib):
     # state placed 2 MiB after it
     assert call(100, (6, p(FAKE + (6 << 33))), (5, p(FAKE + (6 << 33) + (2 << 20)))) == 4
     assert call(1 << 31) == 3
+
+
+def test_binding_rejects_host_tensors():
+    """The binding hands data pointers to GPU kernels, so a host tensor must be
+    refused before the C call (it would pass a host address to a kernel)."""
+    import torch
+    x = torch.zeros((1, 64, 4, 64), dtype=torch.bfloat16)
+    dt = torch.zeros((1, 64, 4))
+    A = torch.zeros(4)
+    Bm = torch.zeros((1, 64, 1, 128), dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="device"):
+        ssd.ssd_chunk_scan(x, dt, A, Bm, Bm, A, 64)
+    with pytest.raises(ValueError, match="device"):
+        ssd.ssd_decode_step(x[:, 0], dt[:, 0], A, Bm[:, 0], Bm[:, 0], A,
+                            torch.zeros((1, 4, 64, 128)))
+    with pytest.raises(ValueError, match="device"):
+        ssd.ssd_state_init(torch.zeros((1, 4, 64, 128)))

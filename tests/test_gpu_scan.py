@@ -28,15 +28,25 @@ def gpu_scan(g, chunk, D=None, init=None, **kw):
     return y, s
 
 
-def full_check(w, Q=None, h0=None, zero_D=True):
-    """GPU scan vs the oracle over the whole input (small workloads)."""
+def full_check(w, Q=None, h0=None, zero_D=True, in_place=False):
+    """GPU scan vs the oracle over the whole input (small workloads).  With
+    in_place, final_state is the initial-state buffer itself (a fresh copy of
+    h0 for each run): the cache resumed in place."""
     Q = Q or w.chunk
     inp = si.prefill_inputs(w)
     g, A, D = gpu_inputs(w, inp)
     wid = widen_inputs(inp, w.io)
     tol = TOL[w.io]
-    init = None if h0 is None else dev(h0.astype(np.float32))
-    y, s = gpu_scan(g, Q, init=init)
+
+    def run(Dv=None):
+        init = None if h0 is None else dev(h0.astype(np.float32))
+        kw = {"final_state": init} if (in_place and init is not None) else {}
+        y, s = gpu_scan(g, Q, D=Dv, init=init, **kw)
+        if kw:
+            assert s.data_ptr() == init.data_ptr()
+        return y, s
+
+    y, s = run()
     h0d = None if h0 is None else h0.astype(np.float32).astype(np.float64)
     yref, sref = oracle.ssd_scan(wid["x"], wid["dt"], A, wid["B"], wid["C"], D, h0=h0d, nthreads=16)
     check_y(host(y), yref, tol)
@@ -44,7 +54,7 @@ def full_check(w, Q=None, h0=None, zero_D=True):
     if zero_D:
         # D masks most of y (|y - D x| is under 1% of |y|); rerun with D = 0 so the
         # SSM part alone is held to the same tolerance.
-        y0, s0 = gpu_scan(g, Q, D=torch.zeros_like(g["D"]), init=init)
+        y0, s0 = run(torch.zeros_like(g["D"]))
         yref0, _ = oracle.ssd_scan(wid["x"], wid["dt"], A, wid["B"], wid["C"], np.zeros_like(D),
                                    h0=h0d, nthreads=16)
         check_y(host(y0), yref0, tol, "y (D = 0)")
@@ -105,47 +115,71 @@ def test_longctx_prefix_fullrun_and_decode_continuity():
     """131072 tokens, 8 groups: (1) the [0, 4096) prefix as its own scan against
     the oracle; (2) the full-length scan on 8 sampled heads against the oracle's
     131072-step recurrence; (3) 256 decode steps from the GPU's final state
-    against the oracle started from that same state."""
+    against the oracle started from that same state.  Each part is run with the
+    workload's D and again with D = 0: D x is about 99% of |y|, so only the
+    D = 0 run holds the scan's own output (entering states of every segment,
+    the intra-chunk and state->output terms) to the tolerance."""
     w = si.WORKLOADS["longctx_2p7b"]
     A, D = si.head_params(w)
+    D0 = np.zeros_like(D)
     tol = TOL[w.io]
     # (1) prefix
     pre = si.prefill_inputs(w, 0, w.prefix)
     gp, _, _ = gpu_inputs(w, pre)
-    yp, sp = gpu_scan(gp, w.chunk)
     wp = widen_inputs(pre, w.io)
-    yref, sref = oracle.ssd_scan(wp["x"], wp["dt"], A, wp["B"], wp["C"], D, nthreads=16)
-    check_y(host(yp), yref, tol, "prefix y")
-    check_state(host(sp), sref, tol, "prefix state")
-    del gp, yp, sp, wp, yref, sref
-    # (2) full length
+    sp = None
+    for Dv, tag in ((D, ""), (D0, " (D = 0)")):
+        yp, sp_v = gpu_scan(gp, w.chunk, D=dev(Dv))
+        yref, sref = oracle.ssd_scan(wp["x"], wp["dt"], A, wp["B"], wp["C"], Dv, nthreads=16)
+        check_y(host(yp), yref, tol, "prefix y" + tag)
+        check_state(host(sp_v), sref, tol, "prefix state" + tag)
+        if sp is not None:
+            assert torch.equal(sp, sp_v), "the state does not depend on D"
+        sp = sp_v
+    del gp, yp, sp, sp_v, wp, yref, sref
+    # (2) full length: the heads sit in 4 of the 8 groups, at both ends of a
+    # group and in the last (two-head) quad of a group's 4 + 4 + 2 split
     inp = si.prefill_inputs(w)
     g, _, _ = gpu_inputs(w, inp)
     y, s = gpu_scan(g, w.chunk)
+    y0, s0 = gpu_scan(g, w.chunk, D=dev(D0))
+    assert torch.equal(s, s0), "the state does not depend on D"
     pairs = [(0, h) for h in (0, 9, 10, 37, 41, 63, 70, 79)]
     yr, sr = oracle_heads(inp, w.io, A, D, pairs)
-    yh, sh = host(y), host(s)
+    yr0, _ = oracle_heads(inp, w.io, A, D0, pairs)
+    yh, y0h, sh = host(y), host(y0), host(s)
     for i, (b, h) in enumerate(pairs):
         assert rel(yh[b, :, h], yr[i]) <= tol, (h, rel(yh[b, :, h], yr[i]))
+        assert rel(y0h[b, :, h], yr0[i]) <= tol, ("D = 0", h, rel(y0h[b, :, h], yr0[i]))
         assert rel(sh[b, h], sr[i]) <= tol, (h, rel(sh[b, h], sr[i]))
-    del g, y, inp
+    # the last 4096 tokens alone: the part of y that the entering states of the
+    # late segments dominate (the full-length norm is spread over 131072 tokens)
+    tail = slice(w.seqlen - 4096, w.seqlen)
+    for i, (b, h) in enumerate(pairs):
+        e = rel(y0h[b, tail, h], yr0[i][tail])
+        assert e <= tol, ("D = 0, last 4096 tokens", h, e)
+    del g, y, y0, s0, inp, yh, y0h
     # (3) decode continuity from the GPU's own final state
     tok = si.decode_tokens(w, w.batch, 0, w.decode_steps)
-    dA, dD = dev(A), dev(D)
-    ys = []
-    s_run = s.clone()
-    for k in range(w.decode_steps):
-        ys.append(ssd.ssd_decode_step(dev(tok["x"][k], w.io), dev(tok["dt"][k]), dA,
-                                      dev(tok["B"][k], w.io), dev(tok["C"][k], w.io), dD, s_run))
-    torch.cuda.synchronize()
-    yd = np.stack([host(t) for t in ys], axis=1)
+    dA = dev(A)
     seq = {"x": si.widen(tok["x"], w.io).transpose(1, 0, 2, 3),
            "dt": tok["dt"].astype(np.float64).transpose(1, 0, 2),
            "B": si.widen(tok["B"], w.io).transpose(1, 0, 2, 3),
            "C": si.widen(tok["C"], w.io).transpose(1, 0, 2, 3)}
-    ydr, sdr = oracle.ssd_scan(seq["x"], seq["dt"], A, seq["B"], seq["C"], D, h0=sh, nthreads=16)
-    check_y(yd, ydr, tol, "decode after long prefill")
-    check_state(host(s_run), sdr, tol, "state after long prefill + decode")
+    for Dv, tag in ((D, ""), (D0, " (D = 0)")):
+        dD = dev(Dv)
+        ys = []
+        s_run = s.clone()
+        for k in range(w.decode_steps):
+            ys.append(ssd.ssd_decode_step(dev(tok["x"][k], w.io), dev(tok["dt"][k]), dA,
+                                          dev(tok["B"][k], w.io), dev(tok["C"][k], w.io), dD,
+                                          s_run))
+        torch.cuda.synchronize()
+        yd = np.stack([host(t) for t in ys], axis=1)
+        ydr, sdr = oracle.ssd_scan(seq["x"], seq["dt"], A, seq["B"], seq["C"], Dv, h0=sh,
+                                   nthreads=16)
+        check_y(yd, ydr, tol, "decode after long prefill" + tag)
+        check_state(host(s_run), sdr, tol, "state after long prefill + decode" + tag)
 
 
 # --------------------------------------------------------------------------
@@ -177,15 +211,18 @@ def test_segment_count_extremes(nseg, monkeypatch):
     full_check(w)
 
 
+@pytest.mark.parametrize("in_place", [False, True])
 @pytest.mark.parametrize("nsub", ["1", "2", "5"])
-def test_state_kernel_units(nsub, monkeypatch):
-    """Segments of the state kernel cut into 1, 2 and 5 units (with a ragged
-    tail and an initial state that the final state aliases)."""
+def test_state_kernel_units(nsub, in_place, monkeypatch):
+    """Segments of the state kernel cut into 1, 2 and 5 units, with a ragged
+    tail and a non-zero initial state; in_place: the final state is written
+    over the initial state (which the state kernel first copies to the spare
+    workspace slot that segment 0 of the scan kernel then reads)."""
     monkeypatch.setenv("SSD_NSEG", "3")
     monkeypatch.setenv("SSD_NSUB", nsub)
     w = si.small_workload(batch=2, seqlen=3 * 640 + 50, nheads=4, chunk=128, seed=21)
     h0 = np.random.default_rng(2).standard_normal((2, 4, 64, 128)).astype(np.float32)
-    full_check(w, h0=h0)
+    full_check(w, h0=h0, in_place=in_place)
 
 
 def test_initial_state_and_split_continuity():
