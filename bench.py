@@ -11,19 +11,25 @@ fresh tokens each step) is reported under ``decode``; batches 1, 16, 64 are
 reported as effective bandwidth (their state fits in the 256 MB MALL or the
 step is launch-bound).  ``decode_steps`` runs the same 1000 steps as one
 ssd_decode_steps launch (state held on-chip across the steps), whose bound is
-fp32 VALU arithmetic.
+fp32 VALU arithmetic.  ``prefill_configs`` holds the 130M-shaped layer and the
+131072-token long-context prefill (8 B/C groups).
 
-The defaults (100 warm-up steps, 100 timed) matter: the GPU's clock ramps up
-over the first ~20 ms of back-to-back work, and a prefill step is 0.3 ms, so a
-short warm-up times the ramp rather than the sustained rate.
+Order: the decode legs and the other prefill configurations run first, then the
+headline's W warm-up steps and its K timed steps.  The GPU's clock ramps up over
+the first ~20 ms of back-to-back work and a prefill step is 0.3 ms, so with a
+short warm-up on an idle GPU the timed steps would measure the ramp rather than
+the sustained rate.
 
 Prints ONE JSON line.  ``roofline`` is the dominant prefill kernel
 (chunk_scan_kernel): algorithmic bytes of the layer per launch / its average
-launch time measured with HIP events on the launch stream; ``decode.roofline``
-likewise for decode_rows_kernel.  ``traffic`` comes from committed rocprofv3
-FETCH_SIZE / WRITE_SIZE counters (profiles/traffic.json) when they were taken
-on the current kernel sources, else null.  ``cpu_baseline`` times the fp64
-oracle (as it stands) on a bounded sample of the same workload.
+launch time measured with HIP events on the launch stream; ``roofline_step``
+the same bytes over the summed times of every kernel of the step;
+``decode.roofline`` likewise for decode_rows_kernel.  ``traffic`` comes from
+committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters (profiles/counters.json)
+when they were taken on the current kernel sources, else null; so does the
+counted MFMA FLOP behind ``mfma.counted``.  ``cpu_baseline`` times the fp64
+oracle (as it stands) on a bounded sample of the same workload, on all the
+CPUs the process may use (at most 16) and on one thread.
 """
 from __future__ import annotations
 
@@ -44,7 +50,7 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s (256 CU x 2.4 GHz x 256 FLOP/clk)
 METRIC = "SSD prefill tokens/s (MFMA %) + decode steps/s (HBM GB/s %) at 2.7B-layer shape"
 CSRC = "state_space_model_mamba_amd/csrc/"
-# the source of each measured kernel; its counters in profiles/traffic.json are
+# the source of each measured kernel; its counters in profiles/counters.json are
 # used while that file and the shared header are unchanged
 KERNEL_SOURCE = {"seg_state_kernel": "ssd_scan_bf16.hip", "chunk_scan_kernel": "ssd_scan_bf16.hip",
                  "decode_rows_kernel": "ssd_decode.hip", "decode_kernel": "ssd_decode.hip",
@@ -96,27 +102,58 @@ def source_digest(kernel: str) -> str:
     return h.hexdigest()
 
 
-def committed_traffic(kernel: str):
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    if not os.path.exists(path):
-        return None
-    rec = json.load(open(path))
-    k = rec.get("kernels", {}).get(kernel)
-    if not k or k.get("source_sha256") != source_digest(kernel):
+COUNTERS = os.path.join(ROOT, "profiles", "counters.json")
+
+
+def _counter_record(kernel: str, wname: str | None):
+    """The committed counter record of a kernel (for workload `wname`, or the
+    first workload that has one), if it was taken on the current sources."""
+    if not os.path.exists(COUNTERS):
+        return None, None
+    rec = json.load(open(COUNTERS))
+    for wl, kernels in rec.get("workloads", {}).items():
+        if wname is not None and wl != wname:
+            continue
+        k = kernels.get(kernel)
+        if k and k.get("source_sha256") == source_digest(kernel):
+            return k, rec
+    return None, None
+
+
+def committed_traffic(kernel: str, wname: str | None = None):
+    k, rec = _counter_record(kernel, wname)
+    if not k or "fetch_bytes" not in k or "write_bytes" not in k:
         return None
     return {"fetch_bytes": k["fetch_bytes"], "write_bytes": k["write_bytes"],
             "total_bytes": k["fetch_bytes"] + k["write_bytes"], "scale": rec.get("copy_scale"),
-            "source": "profiles/traffic.json"}
+            "source": "profiles/counters.json"}
+
+
+def step_traffic(kernels, wname):
+    """Counted HBM bytes of a whole step (every kernel's), if all are current."""
+    parts = [committed_traffic(k, wname) for k in kernels]
+    if any(p is None for p in parts):
+        return None
+    return {"fetch_bytes": sum(p["fetch_bytes"] for p in parts),
+            "write_bytes": sum(p["write_bytes"] for p in parts),
+            "total_bytes": sum(p["total_bytes"] for p in parts),
+            "source": "profiles/counters.json"}
+
+
+def committed_mfma(kernel: str, wname: str):
+    k, _ = _counter_record(kernel, wname)
+    return None if not k or "mfma_flop" not in k else k["mfma_flop"]
 
 
 COPY_KERNEL = "__amd_rocclr_copyBuffer"     # the device copy made by --copy-calibration
 COPY_BYTES = 1 << 30
+KERNELS = ("seg_state_kernel", "chunk_scan_kernel", "decode_rows_kernel", "decode_steps_kernel",
+           "gdn_decode_kernel", "gdn_steps_kernel", "decode_kernel", "scan_f32_kernel")
 
 
 def _counter_means(path, counter):
-    """Per-kernel mean of one rocprofv3 counter (KiB per dispatch) over the
-    dispatches of the kernel's largest grid (the main workload's: the 2.7B
-    prefill, batch 256 for the decode kernels), and the copy total."""
+    """Per-kernel mean of one rocprofv3 counter (per dispatch) over every
+    dispatch of the kernel in the run, and the copy kernel's total."""
     import csv
     per, copy = {}, 0.0
     for r in csv.DictReader(open(path)):
@@ -127,41 +164,41 @@ def _counter_means(path, counter):
         if name.startswith(COPY_KERNEL):
             copy += v
         short = name.split("(")[0].split("::")[-1]
-        for k in ("seg_state_kernel", "chunk_scan_kernel", "decode_rows_kernel",
-                  "decode_steps_kernel", "gdn_decode_kernel", "gdn_steps_kernel",
-                  "decode_kernel", "scan_f32_kernel"):
+        for k in KERNELS:
             if (k in short or k in name) and "multi" not in name:
-                per.setdefault(k, []).append((int(r["Grid_Size"]), v))
+                per.setdefault(k, []).append(v)
                 break
-    means = {}
-    for k, vals in per.items():
-        top = max(g for g, _ in vals)
-        sel = [v for g, v in vals if g == top]
-        means[k] = sum(sel) / len(sel)
-    return means, copy
+    return {k: sum(v) / len(v) for k, v in per.items()}, copy
 
 
-def write_traffic(fetch_csv, write_csv):
-    """profiles/traffic.json from a FETCH_SIZE run and a WRITE_SIZE run of
-    `bench.py --copy-calibration`: each counter is scaled so that the 1 GiB copy
-    reads and writes 1 GiB."""
+def write_counters(wname, fetch_csv, write_csv, mops_csv):
+    """Merge one workload's counters into profiles/counters.json: FETCH_SIZE and
+    WRITE_SIZE (KiB per dispatch) from two runs of `bench.py --copy-calibration`,
+    each scaled so that the 1 GiB copy reads and writes 1 GiB, and
+    SQ_INSTS_VALU_MFMA_MOPS_BF16 (512 FLOP per unit) from a third run."""
     fetch, fcopy = _counter_means(fetch_csv, "FETCH_SIZE")
     write, wcopy = _counter_means(write_csv, "WRITE_SIZE")
+    mops = _counter_means(mops_csv, "SQ_INSTS_VALU_MFMA_MOPS_BF16")[0] if mops_csv else {}
     if fcopy <= 0 or wcopy <= 0:
         raise SystemExit("no copy-calibration dispatches in the counter files")
     fs, ws = COPY_BYTES / (fcopy * 1024), COPY_BYTES / (wcopy * 1024)
-    rec = {"copy_bytes": COPY_BYTES, "copy_scale": {"fetch": fs, "write": ws},
-           "kernels": {k: {"source_sha256": source_digest(k),
-                           "fetch_bytes": fetch[k] * 1024 * fs,
-                           "write_bytes": write.get(k, 0.0) * 1024 * ws,
-                           "fetch_kib_raw": fetch[k], "write_kib_raw": write.get(k, 0.0)}
-                       for k in fetch}}
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    os.makedirs(os.path.dirname(path), exist_ok=True)
-    with open(path, "w") as fh:
-        json.dump(rec, fh, indent=1)
+    rec = json.load(open(COUNTERS)) if os.path.exists(COUNTERS) else {}
+    rec.setdefault("copy_bytes", COPY_BYTES)
+    rec.setdefault("copy_scale", {})[wname] = {"fetch": fs, "write": ws}
+    kernels = {}
+    for k in fetch:
+        kernels[k] = {"source_sha256": source_digest(k),
+                      "fetch_bytes": fetch[k] * 1024 * fs,
+                      "write_bytes": write.get(k, 0.0) * 1024 * ws,
+                      "fetch_kib_raw": fetch[k], "write_kib_raw": write.get(k, 0.0)}
+        if k in mops:
+            kernels[k]["mfma_flop"] = mops[k] * 512
+    rec.setdefault("workloads", {})[wname] = kernels
+    os.makedirs(os.path.dirname(COUNTERS), exist_ok=True)
+    with open(COUNTERS, "w") as fh:
+        json.dump(rec, fh, indent=1, sort_keys=True)
         fh.write("\n")
-    print(json.dumps(rec, indent=1))
+    print(json.dumps({wname: kernels}, indent=1))
 
 
 def to_dev(a, bf16=False):
@@ -171,68 +208,115 @@ def to_dev(a, bf16=False):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def bench_prefill(args):
+PREFILL_WORKLOADS = {
+    "m2_2p7b": "Mamba-2-2.7B-shaped SSD layer prefill (ssd_chunk_scan)",
+    "m2_130m": "Mamba-2-130M-shaped SSD layer prefill (ssd_chunk_scan)",
+    "longctx_2p7b": "long-context prefill at the 2.7B head shape, 8 B/C groups (ssd_chunk_scan)",
+}
+
+
+def prefill_config(w):
+    return {"batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads, "headdim": w.headdim,
+            "dstate": w.dstate, "ngroups": w.ngroups, "chunk": w.chunk, "state": "fp32",
+            "io": "bf16"}
+
+
+def prefill_setup(wname):
+    """A prefill workload's seeded inputs, outputs and workspace, resident in HBM."""
     import torch
 
     import ssd_inputs as si
     import state_space_model_mamba_amd as ssd
 
-    w = si.WORKLOADS["m2_2p7b"]
+    w = si.WORKLOADS[wname]
     A, D = si.head_params(w)
     inp = si.prefill_inputs(w)
-    x, dt = to_dev(inp["x"], True), to_dev(inp["dt"])
-    B, C = to_dev(inp["B"], True), to_dev(inp["C"], True)
-    dA, dD = to_dev(A), to_dev(D)
-    y = torch.empty_like(x)
-    fs = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32, device="cuda")
+    t = {"w": w, "x": to_dev(inp["x"], True), "dt": to_dev(inp["dt"]),
+         "B": to_dev(inp["B"], True), "C": to_dev(inp["C"], True), "A": to_dev(A), "D": to_dev(D)}
+    del inp
+    t["y"] = torch.empty_like(t["x"])
+    t["fs"] = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32,
+                          device="cuda")
     nws = ssd.ssd_chunk_scan_workspace_size(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate,
                                             w.ngroups, w.chunk)
-    ws = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
-    del inp
+    t["ws"] = torch.empty(max(nws, 1), dtype=torch.uint8, device="cuda")
+    return t
+
+
+def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
+    """K timed ssd_chunk_scan calls on one workload (inputs `t` already in HBM)
+    after W untimed ones, then per-kernel HIP-event times (ssd_chunk_scan_timed);
+    with `extras`, the same step with the fused step-size prep.  Only GPU work
+    and its host launches run here, so the clock does not drop between legs."""
+    import torch
+
+    import state_space_model_mamba_amd as ssd
+
+    steps = args.steps if steps is None else steps
+    warmup = args.warmup if warmup is None else warmup
+    w = t["w"]
+    x, dt, B, C, dA, dD = t["x"], t["dt"], t["B"], t["C"], t["A"], t["D"]
+    y, fs, ws = t["y"], t["fs"], t["ws"]
 
     def step():
         ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
+    for _ in range(steps):
         step()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    ev_ms = e0.elapsed_time(e1) / args.steps
-    ms = wall * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / steps
+    ms = wall * 1e3 / steps
 
-    # per-kernel device times, HIP events recorded around each launch on this stream
+    # per-kernel device times: HIP events recorded around each launch on the
+    # stream the kernels run on
     per = {}
-    for _ in range(max(3, min(args.steps, 10))):
+    for _ in range(max(3, min(steps, 10))):
         _, _, times = ssd.ssd_chunk_scan_timed(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs,
                                                workspace=ws)
         for name, t in times:
             per.setdefault(name, []).append(t)
     kern = {k: float(np.mean(v)) for k, v in per.items()}
-    # the same step with the fused step-size prep (dt read as u, softplus(u + bias)
-    # formed in the kernels); u and the bias are arbitrary here, only time matters
-    bias = torch.zeros(w.nheads, dtype=torch.float32, device="cuda")
-    for _ in range(0 if args.no_extras else 3):
-        ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
-                           dt_softplus=True, dt_bias=bias)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(0 if args.no_extras else args.steps):
-        ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
-                           dt_softplus=True, dt_bias=bias)
-    e1.record()
-    torch.cuda.synchronize()
-    sp_ms = None if args.no_extras else e0.elapsed_time(e1) / args.steps
+    sp_ms = None
+    if extras:
+        # the same step with the fused step-size prep (dt read as u, softplus(u +
+        # bias) formed in the kernels); u and the bias are arbitrary here, only
+        # time matters
+        bias = torch.zeros(w.nheads, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
+                               dt_softplus=True, dt_bias=bias)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(steps):
+            ssd.ssd_chunk_scan(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs, workspace=ws,
+                               dt_softplus=True, dt_bias=bias)
+        e1.record()
+        torch.cuda.synchronize()
+        sp_ms = e0.elapsed_time(e1) / steps
     nbytes = prefill_bytes(w)
     flops = prefill_useful_flops(w)
     k3 = kern["chunk_scan_kernel"]
+    step_k = sum(kern.values())
     tokens = w.batch * w.seqlen
+    counted = {k: committed_mfma(k, wname) for k in kern}
+    mfma_counted = None
+    if all(v is not None for v in counted.values()):
+        cf = sum(counted.values())
+        mfma_counted = {"flop_per_step": cf, "achieved_tflops": cf / (step_k * 1e-3) / 1e12,
+                        "frac": cf / (step_k * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+                        "per_kernel": {k: {"flop": v,
+                                           "frac": v / (kern[k] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
+                                       for k, v in counted.items()},
+                        "source": "profiles/counters.json (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 "
+                                  "per launch) over the live kernel times"}
     res = {
         "w": w, "ms": ms, "ev_ms": ev_ms, "tokens_per_s": tokens / (ms * 1e-3),
         "kernels_ms": kern, "bytes": nbytes, "flops": flops,
@@ -240,20 +324,41 @@ def bench_prefill(args):
             "bound": "hbm", "kernel": "chunk_scan_kernel",
             "achieved": nbytes / (k3 * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": nbytes / (k3 * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "traffic": committed_traffic("chunk_scan_kernel"),
+            "traffic": committed_traffic("chunk_scan_kernel", wname),
             "bytes_per_launch": nbytes, "avg_launch_ms": k3,
+        },
+        "roofline_step": {
+            "bound": "hbm", "kernels": sorted(kern),
+            "achieved": nbytes / (step_k * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": nbytes / (step_k * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_step": nbytes, "kernel_ms_per_step": step_k,
+            "traffic": step_traffic(sorted(kern), wname),
+            "note": "the layer's algorithmic bytes over the summed HIP-event times of every "
+                    "kernel of the step",
         },
         "mfma": {
             "useful_gflop_per_step": flops / 1e9,
-            "achieved_tflops": flops / (ms * 1e-3) / 1e12, "peak_tflops": BF16_PEAK_TFLOPS,
-            "frac": flops / (ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
-            "note": "useful (causal-triangle) FLOPs of the whole scan per step time; "
-                    "rocprof MFMA busy counters are in profiles/",
+            "achieved_tflops": flops / (step_k * 1e-3) / 1e12, "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": flops / (step_k * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "counted": mfma_counted,
+            "note": "useful (causal-triangle) FLOPs of the whole scan over the summed kernel "
+                    "times; `counted`: the MFMA FLOPs rocprofv3 counts per launch (committed) "
+                    "over the same live times",
         },
         "path_gbs": nbytes / (ms * 1e-3) / 1e9,
         "dt_softplus_event_ms_per_step": sp_ms,
     }
     return res
+
+
+def prefill_line(pre, wname):
+    """The JSON object of one prefill workload (secondary configs)."""
+    w = pre["w"]
+    return {"workload": PREFILL_WORKLOADS[wname], "config": prefill_config(w),
+            "tokens_per_s": pre["tokens_per_s"], "ms_per_step": pre["ms"],
+            "event_ms_per_step": pre["ev_ms"], "kernels_ms": pre["kernels_ms"],
+            "roofline": pre["roofline"], "roofline_step": pre["roofline_step"],
+            "mfma": pre["mfma"]}
 
 
 def bench_decode(args):
@@ -587,13 +692,39 @@ def bench_noncached(args):
             "rows": rows}
 
 
-def cpu_baseline_prefill(w, npairs=None):
+def host_info():
+    """The host the oracle runs on: logical CPUs of the machine, those this
+    process may run on, and the CPU model."""
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        avail = len(os.sched_getaffinity(0))
+    except AttributeError:
+        avail = os.cpu_count()
+    return {"host_nproc": os.cpu_count(), "cpus_available": avail, "cpu_model": model}
+
+
+def oracle_threads():
+    """Threads for the all-core oracle run: the CPUs this process may use, at
+    most 16 (the CPU share of a one-GPU machine)."""
+    return max(1, min(16, host_info()["cpus_available"] or 1))
+
+
+def cpu_baseline_prefill(w, npairs=None, single_pairs=16):
     """The fp64 oracle on `npairs` of the layer's (batch, head) sequences, full
-    length each, threaded over pairs; tokens/s scaled to the whole layer."""
+    length each, threaded over pairs, and on `single_pairs` of them with one
+    thread (the plain sequential baseline); tokens/s scaled to the whole layer."""
     import oracle
     import ssd_inputs as si
 
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     A, D = si.head_params(w)
     inp = si.prefill_inputs(w)
     H = w.nheads
@@ -601,8 +732,8 @@ def cpu_baseline_prefill(w, npairs=None):
     pairs = [(k // H, k % H) for k in range(npairs)]
     xs = np.stack([si.widen(inp["x"][b, :, h], "bf16") for b, h in pairs])[:, :, None]
     dts = np.stack([inp["dt"][b, :, h] for b, h in pairs]).astype(np.float64)[:, :, None]
-    Bs = np.stack([si.widen(inp["B"][b, :, 0], "bf16") for b, h in pairs])[:, :, None]
-    Cs = np.stack([si.widen(inp["C"][b, :, 0], "bf16") for b, h in pairs])[:, :, None]
+    Bs = np.stack([si.widen(inp["B"][b, :, h // (H // w.ngroups)], "bf16") for b, h in pairs])[:, :, None]
+    Cs = np.stack([si.widen(inp["C"][b, :, h // (H // w.ngroups)], "bf16") for b, h in pairs])[:, :, None]
     del inp
     from concurrent.futures import ThreadPoolExecutor
 
@@ -615,35 +746,59 @@ def cpu_baseline_prefill(w, npairs=None):
     with ThreadPoolExecutor(threads) as ex:
         list(ex.map(one, range(npairs)))
     T = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    for i in range(single_pairs):
+        one(i)
+    T1 = time.perf_counter() - t0
     full_pairs = w.batch * H
     tok_s = (w.batch * w.seqlen) / (T * full_pairs / npairs)
+    tok_s1 = (w.batch * w.seqlen) / (T1 * full_pairs / single_pairs)
     return {"value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
             "sample": f"fp64 oracle on {npairs} of the {full_pairs} (batch, head) sequences of "
                       f"the {w.batch}x{w.seqlen}x{H} layer, all {w.seqlen} tokens each, "
                       f"{threads} threads over sequences; {T:.2f} s wall, tokens/s scaled by "
-                      f"{npairs}/{full_pairs}"}
+                      f"{npairs}/{full_pairs}",
+            "single_thread": {"value": tok_s1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"{single_pairs} of the {full_pairs} sequences, one "
+                                        f"thread; {T1:.2f} s wall, scaled by "
+                                        f"{single_pairs}/{full_pairs}"},
+            **host_info()}
 
 
-def cpu_baseline_decode(w, batch=256, nseq=64, steps=200):
-    """The oracle's decode step on `nseq` sequences for `steps` steps, steps/s
-    scaled to the full batch."""
+def cpu_baseline_decode(w, batch=256, nseq=64, steps=200, single_seq=8):
+    """The oracle's decode step on `nseq` sequences for `steps` steps (threaded
+    over (sequence, head)), and on `single_seq` with one thread; steps/s scaled
+    to the full batch."""
     import oracle
     import ssd_inputs as si
 
-    threads = min(16, os.cpu_count() or 1)
+    threads = oracle_threads()
     A, D = si.head_params(w)
     tok = si.decode_tokens(w, nseq, 0, steps)
-    st = si.random_state(w, nseq).astype(np.float64)
+    st0 = si.random_state(w, nseq).astype(np.float64)
     xs = si.widen(tok["x"], "bf16")
     Bs, Cs = si.widen(tok["B"], "bf16"), si.widen(tok["C"], "bf16")
     dts = tok["dt"].astype(np.float64)
+    st = st0
     t0 = time.perf_counter()
     for k in range(steps):
         _, st = oracle.ssd_decode_step(st, xs[k], dts[k], A, Bs[k], Cs[k], D, nthreads=threads)
     T = time.perf_counter() - t0
+    st = st0[:single_seq]
+    t0 = time.perf_counter()
+    for k in range(steps):
+        _, st = oracle.ssd_decode_step(st, xs[k, :single_seq], dts[k, :single_seq], A,
+                                       Bs[k, :single_seq], Cs[k, :single_seq], D, nthreads=1)
+    T1 = time.perf_counter() - t0
     return {"value": steps / (T * batch / nseq), "unit": "steps/s", "cores": threads,
             "kind": "oracle",
-            "sample": f"{nseq} of {batch} sequences x {steps} steps; scaled by {nseq}/{batch}"}
+            "sample": f"{nseq} of {batch} sequences x {steps} steps, {threads} threads; "
+                      f"{T:.2f} s, scaled by {nseq}/{batch}",
+            "single_thread": {"value": steps / (T1 * batch / single_seq), "unit": "steps/s",
+                              "cores": 1,
+                              "sample": f"{single_seq} of {batch} sequences x {steps} steps, one "
+                                        f"thread; {T1:.2f} s, scaled by {single_seq}/{batch}"},
+            **host_info()}
 
 
 def cpu_baseline_gdn(nseq=32, steps=40, batch=256):
@@ -665,7 +820,48 @@ def cpu_baseline_gdn(nseq=32, steps=40, batch=256):
         T = time.perf_counter() - t0
     return {"value": steps / (T * batch / nseq), "unit": "steps/s", "cores": 1, "kind": "oracle",
             "sample": f"{nseq} of {batch} sequences x {steps} steps, one thread; "
-                      f"{T:.1f} s, scaled by {nseq}/{batch}"}
+                      f"{T:.1f} s, scaled by {nseq}/{batch}", **host_info()}
+
+
+def decode_line(wd, dec):
+    main_b = max(dec)
+    d = dec[main_b]
+    out = {}
+    out["decode"] = {
+        "workload": f"decode_step at the 2.7B shape, state [{main_b},80,64,128] fp32, "
+                    f"{d['steps']} consecutive in-place steps, fresh bf16 tokens",
+        "steps_per_s": d["steps_per_s"], "ms_per_step": d["ms_per_step"],
+        "roofline": {"bound": "hbm", "kernel": "decode_rows_kernel", "achieved": d["gbs"],
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
+                     "traffic": committed_traffic("decode_rows_kernel"),
+                     "bytes_per_launch": d["bytes_per_step"],
+                     "avg_launch_ms": d["event_ms_per_step"]},
+        "batches": {str(b): {k: v for k, v in r.items()} for b, r in sorted(dec.items())},
+        "note": "batch <= 64 keeps the state (<= 168 MB) in the 256 MB MALL or is "
+                "launch-bound: effective bandwidth, not HBM; graph_*: the same steps "
+                "replayed from one captured HIP graph",
+    }
+    fl = decode_steps_flops(main_b, wd)
+    m_ms = d["steps_launch_event_ms_per_step"]
+    out["decode_steps"] = {
+        "workload": f"ssd_decode_steps at the 2.7B shape: the same {d['steps']} steps on a "
+                    f"[{main_b},80,64,128] fp32 state as one launch (state read and written "
+                    f"once, held in registers across the steps)",
+        "steps_per_s": d["steps_launch_steps_per_s"],
+        "ms_per_step": d["steps_launch_ms_per_step"],
+        "roofline": {"bound": "alu", "kernel": "decode_steps_kernel",
+                     "achieved": fl / (m_ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": fl / (m_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                     "traffic": committed_traffic("decode_steps_kernel"),
+                     "flops_per_step": fl, "avg_launch_ms": m_ms * d["steps"]},
+        "batches": {str(b): {"steps_per_s": r["steps_launch_steps_per_s"],
+                             "ms_per_step": r["steps_launch_ms_per_step"],
+                             "event_ms_per_step": r["steps_launch_event_ms_per_step"],
+                             "tflops": r["steps_launch_tflops"]}
+                    for b, r in sorted(dec.items())},
+    }
+    return out
 
 
 def main():
@@ -673,6 +869,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--headline", default="m2_2p7b", choices=sorted(PREFILL_WORKLOADS),
+                    help="the prefill workload of `value` (other choices: counter runs)")
+    ap.add_argument("--secondary", default="m2_130m,longctx_2p7b",
+                    help="further prefill workloads reported under `prefill_configs` ('' = none)")
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--decode-batches", type=str, default="256,64,16,1")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -682,14 +882,20 @@ def main():
                          "and trace runs: every dispatch of a kernel is then the main workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
-    ap.add_argument("--write-traffic", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
-                    help="host only: turn two rocprofv3 counter_collection.csv files "
-                         "(FETCH_SIZE, WRITE_SIZE) into profiles/traffic.json and exit")
+    ap.add_argument("--write-counters", nargs=4, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "MOPS_CSV"),
+                    help="host only: merge three rocprofv3 counter_collection.csv files "
+                         "(FETCH_SIZE, WRITE_SIZE, SQ_INSTS_VALU_MFMA_MOPS_BF16; MOPS_CSV may "
+                         "be '-') into profiles/counters.json under WORKLOAD and exit")
     args = ap.parse_args()
-    if args.write_traffic:
-        write_traffic(*args.write_traffic)
+    if args.write_counters:
+        wl, f, wr, m = args.write_counters
+        write_counters(wl, f, wr, None if m == "-" else m)
         return
     args.decode_batches = [int(v) for v in args.decode_batches.split(",") if v]
+    secondary = [v for v in args.secondary.split(",") if v and v != args.headline]
+    for v in secondary:
+        if v not in PREFILL_WORKLOADS:
+            raise SystemExit(f"unknown prefill workload {v}")
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the SSD hot path here is a single-GPU build "
               "(no sharding or collectives); run with --gpus 1", file=sys.stderr)
@@ -708,7 +914,26 @@ def main():
         dst.copy_(src)                 # reads 1 GiB, writes 1 GiB
         torch.cuda.synchronize()
         del src, dst
-    pre = bench_prefill(args)
+    extra = {}
+    # Every prefill input is generated and moved to HBM first.  The decode half
+    # of the metric and the other prefill configurations run next, then the
+    # headline prefill's warm-up and timed steps, with no host-side gap (input
+    # generation) between the GPU legs.
+    resident = {v: prefill_setup(v) for v in [args.headline] + secondary}
+    if not args.no_decode:
+        wd, dec = bench_decode(args)
+        extra.update(decode_line(wd, dec))
+        if 256 in args.decode_batches:
+            extra["gdn_decode"] = bench_gdn(args)
+    configs = {}
+    for v in secondary:
+        configs[v] = prefill_line(bench_prefill(args, v, resident[v], steps=max(args.steps // 2, 5),
+                                                warmup=max(args.warmup, 5)), v)
+        del resident[v]
+    pre = bench_prefill(args, args.headline, resident[args.headline],
+                        extras=not args.no_extras)
+    del resident
+    torch.cuda.empty_cache()
     w = pre["w"]
     line = {
         "metric": METRIC,
@@ -723,72 +948,33 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "Mamba-2-2.7B-shaped SSD layer prefill (ssd_chunk_scan)",
-                   "batch": w.batch, "seq_len": w.seqlen, "nheads": w.nheads,
-                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
-                   "chunk": w.chunk, "state": "fp32", "io": "bf16"},
+        "config": {"workload": PREFILL_WORKLOADS[args.headline], **prefill_config(w)},
         "event_ms_per_step": pre["ev_ms"],
         "kernels_ms": pre["kernels_ms"],
         "path_gbs": pre["path_gbs"],
         "roofline": pre["roofline"],
+        "roofline_step": pre["roofline_step"],
         "mfma": pre["mfma"],
-        "prefill_fused_dt_softplus": {
+    }
+    if configs:
+        line["prefill_configs"] = configs
+    if not args.no_extras:
+        line["prefill_fused_dt_softplus"] = {
             "event_ms_per_step": pre["dt_softplus_event_ms_per_step"],
             "note": "the same prefill with dt passed as u and softplus(u + dt_bias) formed "
-                    "inside the scan kernels (ssd_dims.flags = SSD_DT_SOFTPLUS)"},
-    }
-    if not args.no_extras:
+                    "inside the scan kernels (ssd_dims.flags = SSD_DT_SOFTPLUS)"}
         line["prefill_varlen"] = bench_varlen(args)
         line["noncached_vs_cached"] = bench_noncached(args)
-    if not args.no_decode:
-        wd, dec = bench_decode(args)
-        main_b = max(dec)
-        d = dec[main_b]
-        line["decode"] = {
-            "workload": f"decode_step at the 2.7B shape, state [{main_b},80,64,128] fp32, "
-                        f"{d['steps']} consecutive in-place steps, fresh bf16 tokens",
-            "steps_per_s": d["steps_per_s"], "ms_per_step": d["ms_per_step"],
-            "roofline": {"bound": "hbm", "kernel": "decode_rows_kernel", "achieved": d["gbs"],
-                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": d["frac"],
-                         "traffic": committed_traffic("decode_rows_kernel"),
-                         "bytes_per_launch": d["bytes_per_step"],
-                         "avg_launch_ms": d["event_ms_per_step"]},
-            "batches": {str(b): {k: v for k, v in r.items()} for b, r in sorted(dec.items())},
-            "note": "batch <= 64 keeps the state (<= 168 MB) in the 256 MB MALL or is "
-                    "launch-bound: effective bandwidth, not HBM; graph_*: the same steps "
-                    "replayed from one captured HIP graph",
-        }
-        fl = decode_steps_flops(main_b, wd)
-        m_ms = d["steps_launch_event_ms_per_step"]
-        line["decode_steps"] = {
-            "workload": f"ssd_decode_steps at the 2.7B shape: the same {d['steps']} steps on a "
-                        f"[{main_b},80,64,128] fp32 state as one launch (state read and written "
-                        f"once, held in registers across the steps)",
-            "steps_per_s": d["steps_launch_steps_per_s"],
-            "ms_per_step": d["steps_launch_ms_per_step"],
-            "roofline": {"bound": "alu", "kernel": "decode_steps_kernel",
-                         "achieved": fl / (m_ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
-                         "unit": "TFLOP/s",
-                         "frac": fl / (m_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
-                         "traffic": committed_traffic("decode_steps_kernel"),
-                         "flops_per_step": fl, "avg_launch_ms": m_ms * d["steps"]},
-            "batches": {str(b): {"steps_per_s": r["steps_launch_steps_per_s"],
-                                 "ms_per_step": r["steps_launch_ms_per_step"],
-                                 "event_ms_per_step": r["steps_launch_event_ms_per_step"],
-                                 "tflops": r["steps_launch_tflops"]}
-                        for b, r in sorted(dec.items())},
-        }
-        if 256 in args.decode_batches:
-            line["gdn_decode"] = bench_gdn(args)
-        if not args.no_cpu_baseline:
-            if "gdn_decode" in line:
-                line["gdn_decode"]["cpu_baseline"] = cpu_baseline_gdn()
+    line.update(extra)
+    if not args.no_cpu_baseline:
+        if "gdn_decode" in line:
+            line["gdn_decode"]["cpu_baseline"] = cpu_baseline_gdn()
+        if "decode" in line:
             line["decode"]["cpu_baseline"] = cpu_baseline_decode(wd)
             line["decode_steps"]["cpu_baseline"] = dict(
                 line["decode"]["cpu_baseline"],
                 sample=line["decode"]["cpu_baseline"]["sample"] + " (the oracle has one decode "
                        "form: the same run serves both)")
-    if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(w)
     print(json.dumps(line), flush=True)
 
