@@ -148,6 +148,30 @@ ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const float *dt, 
                           void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * ssd_chunk_scan_noalloc -- ssd_chunk_scan without a workspace argument, for
+ * callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc.  It allocates nothing
+ * (no hipMalloc, no hipFree, no allocating library call); the workspace is a
+ * scratch array inside the library, SSD_NOALLOC_SCRATCH_BYTES per device,
+ * which each device the library runs on holds from its first call there until
+ * the process ends.  The caller still passes every input and output.
+ *   Arguments, shapes, results and errors as for ssd_chunk_scan (the same
+ *   plan and kernels: the results are identical to ssd_chunk_scan's).
+ *   SSD_ERR_WORKSPACE, before any device call, when the workspace that
+ *   ssd_chunk_scan_workspace_size reports for dims exceeds
+ *   SSD_NOALLOC_SCRATCH_BYTES (use ssd_chunk_scan with a caller workspace).
+ * Every call on one device shares that device's scratch array, which keeps the
+ * last call's contents (nothing in it needs to start at zero): calls that can
+ * overlap in time on one device (other streams, other threads) race on it and
+ * must be ordered by the caller.  The stream must belong to the current device.
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+ssd_status ssd_chunk_scan_noalloc(const ssd_dims *dims, const void *x, const float *dt,
+                                  const float *A, const void *B, const void *C, const float *D,
+                                  const float *initial_state, void *y, float *final_state,
+                                  void *stream);
+
+/*
  * ssd_chunk_scan_varlen -- prefill of a packed batch of sequences of
  * different lengths, each its own recurrence with its own cache (section 2 of
  * the page, per sequence, as ssd_chunk_scan).  dims->batch = number of sequences S, dims->seqlen = total

@@ -14,6 +14,7 @@ to pass u instead of dt; the step size is then softplus(u + dt_bias) in the kern
     ssd_decode_step(x, dt, A, B, C, D, state, y=None) -> y
     ssd_decode_steps(x, dt, A, B, C, D, state, y=None) -> y   (S steps in one launch)
     ssd_chunk_scan_timed(...) -> (y, final_state, [(kernel, ms), ...])
+    ssd_chunk_scan_noalloc(x, dt, A, B, C, D, chunk, ...) -> (y, final_state)  (no workspace)
     ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, ...) -> (y, final_states)
     ssd_gdn_decode_step(q, k, v, g, beta, state, o=None) -> o   (Gated DeltaNet step)
     ssd_gdn_decode_steps(q, k, v, g, beta, state, o=None) -> o  (S steps in one launch)
@@ -33,7 +34,8 @@ STATUS = {0: "SSD_OK", 1: "SSD_ERR_NULL", 2: "SSD_ERR_SHAPE", 3: "SSD_ERR_UNSUPP
 EXPORTS = ("ssd_status_string", "ssd_version", "ssd_state_init", "ssd_chunk_scan_workspace_size",
            "ssd_chunk_scan", "ssd_decode_step", "ssd_decode_steps", "ssd_chunk_scan_timed",
            "ssd_chunk_scan_varlen_workspace_size", "ssd_chunk_scan_varlen",
-           "ssd_gdn_decode_step", "ssd_gdn_decode_steps")
+           "ssd_gdn_decode_step", "ssd_gdn_decode_steps", "ssd_chunk_scan_noalloc")
+NOALLOC_SCRATCH_BYTES = 96 << 20   # SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h
 
 
 class SsdError(RuntimeError):
@@ -86,6 +88,8 @@ def load(path: str | None = None):
                                           ctypes.POINTER(ctypes.c_char_p),
                                           ctypes.POINTER(ctypes.c_int)])
     lib.ssd_chunk_scan_timed.restype = ctypes.c_int
+    lib.ssd_chunk_scan_noalloc.argtypes = [dims] + [vp] * 10
+    lib.ssd_chunk_scan_noalloc.restype = ctypes.c_int
     lib.ssd_decode_step.argtypes = [dims] + [vp] * 9
     lib.ssd_decode_step.restype = ctypes.c_int
     lib.ssd_decode_steps.argtypes = [dims, ctypes.c_int64] + [vp] * 9
@@ -203,7 +207,7 @@ def ssd_state_init(state, src=None, stream=None):
 
 
 def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
-               dt_softplus=False, dt_bias=None, stream=None):
+               dt_softplus=False, dt_bias=None, stream=None, need_workspace=True):
     import torch
     dev = _device_of(x)
     if x.dim() != 4 or B.dim() != 4:
@@ -224,7 +228,7 @@ def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspac
     _need("workspace", workspace, dev, optional=True)
     _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(bsz, L, H, P, N, G, chunk, io, dt_softplus, dt_bias)
-    need = ssd_chunk_scan_workspace_size(bsz, L, H, P, N, G, chunk, io)
+    need = ssd_chunk_scan_workspace_size(bsz, L, H, P, N, G, chunk, io) if need_workspace else 0
     # outputs and workspace come from the allocator on the call's own stream, so
     # that their blocks are not handed to other work while the kernels run
     with torch.cuda.stream(_stream_obj(stream, dev)):
@@ -246,6 +250,18 @@ def ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_s
     args, y, fs, ws = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state,
                                  workspace, dt_softplus, dt_bias, stream)
     _check("ssd_chunk_scan", load().ssd_chunk_scan(*args, _stream(stream)))
+    return y, fs
+
+
+def ssd_chunk_scan_noalloc(x, dt, A, B, C, D, chunk, initial_state=None, y=None,
+                           final_state=None, stream=None, dt_softplus=False, dt_bias=None):
+    """ssd_chunk_scan with the library's own per-device scratch array as its
+    workspace (nothing is allocated by the library; pass y and final_state to
+    allocate nothing here either).  Calls that overlap in time on one device
+    race on the scratch array.  Returns (y, final_state)."""
+    args, y, fs, _ = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, None,
+                                dt_softplus, dt_bias, stream, need_workspace=False)
+    _check("ssd_chunk_scan_noalloc", load().ssd_chunk_scan_noalloc(*args[:10], _stream(stream)))
     return y, fs
 
 

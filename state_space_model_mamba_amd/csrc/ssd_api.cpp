@@ -4,6 +4,7 @@
 
 #include <algorithm>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "ssd.h"
@@ -475,7 +476,7 @@ SSD_EXPORT const char *ssd_status_string(ssd_status status)
 
 SSD_EXPORT int ssd_version(void)
 {
-    return 10100;
+    return 10200;
 }
 
 SSD_EXPORT ssd_status ssd_state_init(const ssd_dims *dims, float *state, const float *src,
@@ -518,6 +519,66 @@ SSD_EXPORT ssd_status ssd_chunk_scan(const ssd_dims *dims, const void *x, const 
 {
     return run_scan(dims, x, dt, A, B, C, D, initial_state, y, final_state, workspace,
                     workspace_bytes, static_cast<hipStream_t>(stream), nullptr);
+}
+
+namespace {
+
+// Scratch memory of ssd_chunk_scan_noalloc: the scan's workspace (unit states
+// and their decays) for callers that cannot allocate.  Each device the library
+// runs on holds its own copy from the library's first use there until the
+// process ends.  Host code never names the array except to look up its device
+// address: in host code the name is a host-side stand-in, and a kernel handed
+// it would fault.
+constexpr size_t kScratchBytes = SSD_NOALLOC_SCRATCH_BYTES;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_addr[kMaxDevices];   // per device, set once (guarded by scratch_mu)
+
+// The device address of the current device's scratch array, looked up the first
+// time a call runs on that device.
+ssd_status scratch_for_current_device(void **out)
+{
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0)
+        return SSD_ERR_DEVICE;
+    if (dev >= kMaxDevices)
+        return SSD_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(scratch_mu);
+    if (!scratch_addr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p)
+            return SSD_ERR_DEVICE;
+        scratch_addr[dev] = p;
+    }
+    *out = scratch_addr[dev];
+    return SSD_OK;
+}
+
+}  // namespace
+
+SSD_EXPORT ssd_status ssd_chunk_scan_noalloc(const ssd_dims *dims, const void *x, const float *dt,
+                                             const float *A, const void *B, const void *C,
+                                             const float *D, const float *initial_state, void *y,
+                                             float *final_state, void *stream)
+{
+    ssd_status st = check_dims(dims, true);
+    if (st != SSD_OK)
+        return st;
+    if ((st = scan_supported(dims)) != SSD_OK)
+        return st;
+    // the same plan as ssd_chunk_scan, so the same kernels and the same results;
+    // a plan whose workspace exceeds the scratch array is refused before any
+    // device call
+    const size_t need = scan_workspace(dims);
+    if (need > kScratchBytes)
+        return SSD_ERR_WORKSPACE;
+    void *ws = nullptr;
+    if (need > 0 && (st = scratch_for_current_device(&ws)) != SSD_OK)
+        return st;
+    return run_scan(dims, x, dt, A, B, C, D, initial_state, y, final_state, ws,
+                    need > 0 ? kScratchBytes : 0, static_cast<hipStream_t>(stream), nullptr);
 }
 
 SSD_EXPORT ssd_status ssd_chunk_scan_timed(const ssd_dims *dims, const void *x, const float *dt,

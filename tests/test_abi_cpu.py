@@ -31,7 +31,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == set(ssd.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
-    assert lib.ssd_version() == 10100
+    assert lib.ssd_version() == 10200
 
 
 def test_status_strings(lib):
@@ -298,3 +298,17 @@ def test_binding_rejects_host_tensors():
                             torch.zeros((1, 4, 64, 128)))
     with pytest.raises(ValueError, match="device"):
         ssd.ssd_state_init(torch.zeros((1, 4, 64, 128)))
+
+
+def test_noalloc_rejects_workspace_beyond_scratch(lib):
+    """A problem whose workspace exceeds the no-alloc scratch array is refused
+    with SSD_ERR_WORKSPACE before any device call (the pointers are never used)."""
+    d = ssd.make_dims(16, 16384, 80, 64, 128, 1, 256, ssd.SSD_BF16)
+    need = ssd.ssd_chunk_scan_workspace_size(16, 16384, 80, 64, 128, 1, 256)
+    assert need > ssd.NOALLOC_SCRATCH_BYTES
+    p = [ctypes.c_void_p(0x100000 * (i + 1)) for i in range(9)]
+    assert lib.ssd_chunk_scan_noalloc(ctypes.byref(d), *p, None) == 5
+    # unsupported shapes and bad dims are refused the same way
+    d.headdim = 32
+    assert lib.ssd_chunk_scan_noalloc(ctypes.byref(d), *p, None) == 3
+    assert lib.ssd_chunk_scan_noalloc(None, *p, None) == 1
