@@ -40,8 +40,15 @@
  *     aligned (x and y of ssd_decode_step(s): element-aligned); dt, A, D
  *     4-byte.  Otherwise SSD_ERR_ALIGNMENT.
  *   - Float inputs must be finite.  Outputs for non-finite inputs are undefined.
- *   - The library holds no global state; calls on different streams may run
- *     concurrently if their buffers do not overlap.
+ *   - State kept between calls: each host thread caches its last eight
+ *     variable-length launch plans (a pure function of the sizes, so results
+ *     never depend on it), and ssd_chunk_scan_noalloc keeps one scratch
+ *     array per device.  Apart from ssd_chunk_scan_noalloc (see there), calls
+ *     on different streams may run concurrently if their buffers do not
+ *     overlap.
+ *   - Environment: SSD_NSEG and SSD_NSUB, when set to positive integers,
+ *     override the bf16 scan's segment and unit counts (a test hook: the
+ *     result changes only by rounding, the workspace size with the plan).
  *   - Shapes (x, y : [B, L, H, P] of io_dtype; dt : [B, L, H] fp32;
  *     A, D : [H] fp32; B, C : [B, L, G, N] of io_dtype;
  *     state : [B, H, P, N] fp32, n fastest).

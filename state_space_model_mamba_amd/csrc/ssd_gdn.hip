@@ -40,6 +40,7 @@ template <> __device__ __forceinline__ __bf16 gdn_t<__bf16>(float v) { return (_
 constexpr int64_t kGdnNTBytes = 256ll << 20;
 
 typedef float gdn_f4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4_t __attribute__((ext_vector_type(4)));
 
 template <bool kNT>
 __device__ __forceinline__ float4 gdn_ld(const float *p)
@@ -190,28 +191,36 @@ __global__ __launch_bounds__(kGdnThreads) void gdn_decode_kernel(
 // SIMD (128 VGPRs, no spill inside the step loop; the compiler alone took 160
 // and three waves, 18% slower at batch 256); smaller slices need fewer
 // registers anyway.
-template <typename T, int DK, int CT>
-__global__ __launch_bounds__(kGdnThreads) __attribute__((amdgpu_waves_per_eu(DK * CT <= 128 * 128 ? 4 : 1)))
+// NH value heads of one query/key head per work-group (NH = 2 when the value
+// heads per query/key head come in pairs; section 2C of the page: the two
+// value heads of a pair share the q/k datapath).  Waves 4 h .. 4 h + 3 serve
+// value head h of the group; q and k are fetched once per step for all of
+// them, and q . k is formed once.
+template <typename T, int DK, int CT, int NH>
+__global__ __launch_bounds__(kGdnThreads * NH) __attribute__((amdgpu_waves_per_eu(DK * CT <= 128 * 128 ? 4 : 1)))
 void gdn_steps_kernel(
     int nsteps, int Bn, int Hk, int Hv, int dv, const T *__restrict__ q,
     const T *__restrict__ k, const T *__restrict__ v, const float *__restrict__ g,
     const float *__restrict__ beta, float *__restrict__ state, T *__restrict__ o)
 {
+    constexpr int kThreads = kGdnThreads * NH;
     constexpr int LPR = CT / 4, RPI = 64 / LPR, ROWS = DK / (4 * RPI);
     static_assert(ROWS >= 1 && ROWS * 4 * RPI == DK, "DK rows split over 4 waves x RPI");
-    constexpr int QK = DK / kGdnThreads > 0 ? DK / kGdnThreads : 1;   // q/k elements per thread
+    constexpr int QK = DK / kThreads > 0 ? DK / kThreads : 1;   // q/k elements per thread
     // q and k in three buffers (step t reads t % 3 and writes step t + 1's
     // into the next); the partials and q . k in two (by step parity)
     __shared__ float sk[3][DK], sq[3][DK];
-    __shared__ float4 part[2][4][LPR][2];   // per wave: r (row group 0) and p (row group 1)
+    __shared__ float4 part[2][NH][4][LPR][2];   // per wave: r (row group 0) and p (row group 1)
     static_assert(RPI == 2 || RPI == 4, "row groups of a wave on lane bit 5 (and 4)");
     __shared__ float sqk[2];
 
     const int tiles = dv / CT;
-    const int bj = blockIdx.x / tiles, tile = blockIdx.x - bj * tiles;
-    const int b = bj / Hv, j = bj - b * Hv, i = j / (Hv / Hk);
+    const int bp = blockIdx.x / tiles, tile = blockIdx.x - bp * tiles;   // (b, head group)
     const int tid = threadIdx.x;
-    const int w = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+    const int wg = __builtin_amdgcn_readfirstlane(tid / 64), lane = tid % 64;
+    const int hs = wg / 4, w = wg % 4;                   // value head in the group, wave of its four
+    const int b = bp / (Hv / NH), j = (bp - b * (Hv / NH)) * NH + hs, i = j / (Hv / Hk);
+    const int bj = b * Hv + j;
     const int lg = lane / LPR, lc = lane % LPR;
     const int c0 = tile * CT + 4 * lc;
     const int r0 = (w * RPI + lg) * ROWS;
@@ -220,11 +229,17 @@ void gdn_steps_kernel(
     const T *vb = v + (int64_t)bj * dv + c0;
     T *ob = o + (int64_t)bj * dv + c0;
 
-    float *S = state + ((int64_t)bj * DK + r0) * dv + c0;
+    // The value head's state block through a buffer resource: one 32-bit lane
+    // offset, the row stride in the scalar offset, so that no per-row address
+    // stays live across the step loop for the final store.
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        state + (int64_t)bj * DK * dv, (short)0, DK * dv * 4, 0x00020000);
+    const unsigned soff = ((unsigned)r0 * (unsigned)dv + (unsigned)c0) * 4u;
     float4 s[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r)
-        s[r] = *reinterpret_cast<const float4 *>(S + (int64_t)r * dv);
+        s[r] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              srs, soff, r * dv * 4, 0));
 
     // A step's q and k (this thread's share, for the LDS copy), fetched two
     // steps ahead since they go to LDS one step ahead; its v (this thread's
@@ -239,7 +254,7 @@ void gdn_steps_kernel(
         const int64_t tt = t < nsteps ? t : nsteps - 1;
 #pragma unroll
         for (int e = 0; e < QK; ++e) {
-            const int idx = tid + e * kGdnThreads;
+            const int idx = tid + e * kThreads;
             in.qv[e] = idx < DK ? gdn_f<T>(qb[tt * qks + idx]) : 0.f;
             in.kv[e] = idx < DK ? gdn_f<T>(kb[tt * qks + idx]) : 0.f;
         }
@@ -255,7 +270,7 @@ void gdn_steps_kernel(
     auto put_qk = [&](const QkIn &in, int buf) {
 #pragma unroll
         for (int e = 0; e < QK; ++e) {
-            const int idx = tid + e * kGdnThreads;
+            const int idx = tid + e * kThreads;
             if (idx < DK) {
                 sq[buf][idx] = in.qv[e];
                 sk[buf][idx] = in.kv[e];
@@ -301,10 +316,10 @@ void gdn_steps_kernel(
         wave_sum(pr);
         wave_sum(pp);
         if (lg == 0)
-            part[hb][w][lc][0] = pr;
+            part[hb][hs][w][lc][0] = pr;
         else if (lg == 1)
-            part[hb][w][lc][1] = pp;
-        if (w == 1) {   // q . k (wave 1, so wave 0 is free for the delta below)
+            part[hb][hs][w][lc][1] = pp;
+        if (wg == 1) {   // q . k, once for the group (wave 1, so wave 0 is free for the delta below)
             float d = 0.f;
 #pragma unroll
             for (int e = lane; e < DK; e += 64)
@@ -316,10 +331,10 @@ void gdn_steps_kernel(
                 sqk[hb] = d;
         }
         __syncthreads();   // partials, q . k and step t + 1's q, k in LDS
-        float4 R = part[hb][0][lc][0], Pq = part[hb][0][lc][1];
+        float4 R = part[hb][hs][0][lc][0], Pq = part[hb][hs][0][lc][1];
 #pragma unroll
         for (int m = 1; m < 4; ++m) {
-            const float4 a = part[hb][m][lc][0], c = part[hb][m][lc][1];
+            const float4 a = part[hb][hs][m][lc][0], c = part[hb][hs][m][lc][1];
             R.x += a.x; R.y += a.y; R.z += a.z; R.w += a.w;
             Pq.x += c.x; Pq.y += c.y; Pq.z += c.z; Pq.w += c.w;
         }
@@ -330,7 +345,7 @@ void gdn_steps_kernel(
         d.y = cur.bb * (cur.vv[1] - cur.gg * R.y);
         d.z = cur.bb * (cur.vv[2] - cur.gg * R.z);
         d.w = cur.bb * (cur.vv[3] - cur.gg * R.w);
-        if (tid < LPR) {
+        if (w == 0 && lane < LPR) {
             T *oj = ob + (int64_t)t * vs;
             const float qk = sqk[hb];
             oj[0] = gdn_t<T>(cur.gg * Pq.x + qk * d.x);
@@ -361,8 +376,34 @@ void gdn_steps_kernel(
     }
 #pragma unroll
     for (int r = 0; r < ROWS; ++r)
-        *reinterpret_cast<float4 *>(S + (int64_t)r * dv) =
-            make_float4(s[r].x * sc, s[r].y * sc, s[r].z * sc, s[r].w * sc);
+        __builtin_amdgcn_raw_buffer_store_b128(
+            __builtin_bit_cast(u32x4_t, make_float4(s[r].x * sc, s[r].y * sc, s[r].z * sc, s[r].w * sc)),
+            srs, soff, r * dv * 4, 0);
+}
+
+template <typename T, int DK, int CT>
+hipError_t gdn_steps_launch(int64_t S, int64_t B, int64_t Hk, int64_t Hv, int64_t dv,
+                            const void *q, const void *k, const void *v, const float *g,
+                            const float *beta, float *state, void *o, hipStream_t s)
+{
+    const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
+            *vv = static_cast<const T *>(v);
+    T *oo = static_cast<T *>(o);
+    const int n = (int)S, b = (int)B, hk = (int)Hk, hv = (int)Hv, d = (int)dv;
+    // value heads in pairs when every query/key head has an even number of
+    // them and the pairs still give every CU a work-group (a small batch is
+    // latency-bound per step, and twice the work-groups of one value head each
+    // finish a step sooner)
+    if ((Hv / Hk) % 2 == 0 && B * (Hv / 2) * (dv / CT) >= 256) {
+        const unsigned grid = (unsigned)(B * (Hv / 2) * (dv / CT));
+        gdn_steps_kernel<T, DK, CT, 2><<<grid, 2 * kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv,
+                                                                         g, beta, state, oo);
+    } else {
+        const unsigned grid = (unsigned)(B * Hv * (dv / CT));
+        gdn_steps_kernel<T, DK, CT, 1><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv, g,
+                                                                     beta, state, oo);
+    }
+    return hipGetLastError();
 }
 
 template <typename T, int DK>
@@ -373,24 +414,13 @@ hipError_t gdn_steps_dispatch_dv(int64_t S, int64_t B, int64_t Hk, int64_t Hv, i
     // 64-column tiles at dk = 256, so that a thread holds 64 state elements
     // and the kernel runs four waves per SIMD (128-column tiles: 128 elements,
     // 256 VGPRs, one wave)
-    const int64_t ct = (dv < 128 || DK == 256) ? 64 : 128;
-    const unsigned grid = (unsigned)(B * Hv * (dv / ct));
-    const T *qq = static_cast<const T *>(q), *kk = static_cast<const T *>(k),
-            *vv = static_cast<const T *>(v);
-    T *oo = static_cast<T *>(o);
-    const int n = (int)S, b = (int)B, hk = (int)Hk, hv = (int)Hv, d = (int)dv;
     if constexpr (DK == 256) {
-        gdn_steps_kernel<T, DK, 64><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv, g,
-                                                                 beta, state, oo);
+        return gdn_steps_launch<T, DK, 64>(S, B, Hk, Hv, dv, q, k, v, g, beta, state, o, s);
     } else {
-        if (ct == 64)
-            gdn_steps_kernel<T, DK, 64><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk, vv,
-                                                                     g, beta, state, oo);
-        else
-            gdn_steps_kernel<T, DK, 128><<<grid, kGdnThreads, 0, s>>>(n, b, hk, hv, d, qq, kk,
-                                                                      vv, g, beta, state, oo);
+        if (dv < 128)
+            return gdn_steps_launch<T, DK, 64>(S, B, Hk, Hv, dv, q, k, v, g, beta, state, o, s);
+        return gdn_steps_launch<T, DK, 128>(S, B, Hk, Hv, dv, q, k, v, g, beta, state, o, s);
     }
-    return hipGetLastError();
 }
 
 template <typename T>

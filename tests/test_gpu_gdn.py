@@ -117,12 +117,29 @@ def test_gdn_steps_page_shape(io, batch, steps):
 
 
 @pytest.mark.parametrize("dk,dv,Hk,Hv", [(64, 64, 2, 2), (256, 64, 3, 6), (256, 256, 2, 4),
-                                         (64, 256, 1, 4)])
+                                         (64, 256, 1, 4), (128, 128, 2, 6)])
 def test_gdn_steps_shapes(dk, dv, Hk, Hv):
+    """Value heads per query/key head 1 and 3 (one value head per work-group)
+    and 2 and 4 (pairs of value heads sharing the q/k datapath)."""
     tok = si.gdn_tokens(dk + 3 * dv + Hk, 6, 2, Hk, Hv, dk, dv, "bf16")
     o, s = run_steps_launch(tok, "bf16")
     oref, sref = oracle_run(tok, "bf16")
     check(o, s, oref, sref, TOL["bf16"], f"gdn steps dk={dk} dv={dv}")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+@pytest.mark.parametrize("dk,dv,Hk,Hv,batch", [(128, 128, 16, 32, 16), (64, 256, 1, 4, 64),
+                                               (256, 64, 3, 6, 86)])
+def test_gdn_steps_value_head_pairs(io, dk, dv, Hk, Hv, batch):
+    """Batches large enough that the launch pairs the value heads of each
+    query/key head in one work-group (the pairs fill every CU), against the
+    oracle: the page's shape, four value heads per query/key head over two
+    128-column tiles, and dk = 256 on 64-column tiles."""
+    steps = 7
+    tok = si.gdn_tokens(600 + dk + dv + batch, steps, batch, Hk, Hv, dk, dv, io)
+    o, s = run_steps_launch(tok, io)
+    oref, sref = oracle_run(tok, io)
+    check(o, s, oref, sref, TOL[io], f"gdn steps pairs {io} dk={dk} dv={dv} b={batch}")
 
 
 def test_gdn_steps_zero_steps():
