@@ -24,11 +24,14 @@ hipError_t log_kernel(EventLog *log, const char *name, hipStream_t s);
 // Step-size prep fused into the kernels: with softplus set, the dt argument
 // holds u and the step size of head h is softplus(u + bias[h]) (bias NULL: 0),
 // evaluated in fp32 as max(v, 0) + log1p(exp(-|v|)), which neither overflows
-// for large v nor loses the small values of very negative v.  log1p(e) is
-// log(1 + e) * e / ((1 + e) - 1), which cancels the rounding of 1 + e (D.
-// Goldberg, "What every computer scientist should know about floating-point
-// arithmetic", 1991, theorem 4), on the hardware exp2 / log2: a few ulp.
-// Positions past the end of a sequence keep a step size of 0.
+// for large v nor loses the small values of very negative v.  With
+// w = fl(1 + e), log1p(e) = log(w) - log(w / (1 + e)), and the rounding error
+// d = (w - 1) - e is exact in fp32 (w - 1 is exact for w in [1, 2], and so is
+// the difference of the two nearby values), so log1p(e) = log(w) - d / (1 + e)
+// to first order in d.  Dropping the 1 / (1 + e) changes the result by at most
+// |d| e <= 2^-24 e, i.e. 2^-24 of log1p(e) ~ e: no reciprocal, and w = 1
+// (e below 2^-24) needs no branch (d = -e).  The exp and log are the hardware
+// exp2 / log2.  Positions past the end of a sequence keep a step size of 0.
 struct DtPrep {
     const float *bias;
     int softplus;
@@ -39,8 +42,8 @@ __device__ __forceinline__ float softplus_dt(float u, float bias)
     const float v = u + bias;
     const float e = __expf(-fabsf(v));   // (0, 1]
     const float w = 1.f + e;
-    const float l = w == 1.f ? e : __logf(w) * (e * __builtin_amdgcn_rcpf(w - 1.f));
-    return fmaxf(v, 0.f) + l;
+    const float d = (w - 1.f) - e;       // the rounding error of 1 + e, exactly
+    return fmaxf(v, 0.f) + (__logf(w) - d);
 }
 
 // Sum of a wave value with its partner lane across lane bit 4 or 5 (the lane

@@ -337,6 +337,11 @@ __device__ __forceinline__ void load_tile(Prefetch<kH> &pf, const WaveIo &io, in
     const int l = tid & 63, pt = tid & 127;
     const int64_t rows = L - t0;
     if constexpr ((kPart & 1) != 0) {
+        // dt first: it is consumed mid-tile (the fused step-size prep) while
+        // the B and C loads issued after it may still be in flight
+        const unsigned dp = (unsigned)io.dtstride * 4u;
+        const rsrc_t rd = tile_rsrc(io.dt + t0 * io.dtstride, rows, dp, 4);
+        pf.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (unsigned)l * dp, 0, 0));
         const unsigned bp = (unsigned)io.bstride * 2u;
         const rsrc_t rb = tile_rsrc(io.B + t0 * io.bstride, rows, bp, kN * 2);
 #pragma unroll
@@ -350,9 +355,6 @@ __device__ __forceinline__ void load_tile(Prefetch<kH> &pf, const WaveIo &io, in
             const unsigned off = (unsigned)((tid >> 4) + kRows * r) * bp + (tid & 15) * 16u;
             pf.c[r] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(rc, off, 0, 0));
         }
-        const unsigned dp = (unsigned)io.dtstride * 4u;
-        const rsrc_t rd = tile_rsrc(io.dt + t0 * io.dtstride, rows, dp, 4);
-        pf.dt = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rd, (unsigned)l * dp, 0, 0));
     }
     if constexpr ((kPart & 2) != 0) {
         const unsigned xp = (unsigned)io.xstride * 2u;
@@ -498,9 +500,9 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &p
         *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow +
                                    (((pt & 7) ^ xswz(row)) << 4)) = pf.x[r];
     }
-    float dtl = pf.dt;
-    if constexpr (kSp)   // the step size from u; tokens past the end keep 0
-        dtl = l < L - t0 ? softplus_dt(dtl, dtb) : 0.f;
+    // (with the fused step-size prep, pf.dt already holds softplus(u + bias),
+    // formed by prep_dt while the previous tile was computed)
+    const float dtl = pf.dt;
     const float lam = wave_inclusive_sum(dtl * Ah2, l);
     // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
     // hold the same sum only up to the summation order, which matters when
@@ -517,6 +519,15 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &p
     sm.dtv[w][l] = dtl;
     sm.vt[w][l] = fast_exp2(lq - lam) * dtl;
     return md;
+}
+
+// The fused step-size prep on a prefetched tile at t0 (lane = token): the
+// step size from u, tokens past the end L keep 0.
+template <int kH, bool kSp>
+__device__ __forceinline__ void prep_dt(Prefetch<kH> &pf, int64_t t0, int64_t L, float dtb, int l)
+{
+    if constexpr (kSp)
+        pf.dt = l < L - t0 ? softplus_dt(pf.dt, dtb) : 0.f;
 }
 
 // The scan kernel: y of segment `seg` from the state entering it and, for the
@@ -674,6 +685,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                     Y[q][tb] *= dec;
             }
             lds_barrier();                            // every block of the tile is in Gs
+            // the next tile's step sizes, well before they are staged
+            prep_dt<kH, kSp>(pf, t0 + kT, tseg1, dtb, l);
             // Mask and decay, B-operand over tokens s (slot 4 h + i <-> s = 32 jj + 16 h + 4 g + i):
             //   s in an earlier 16-block: exp(Lam_t - Lam_q) * [exp(Lam_q - Lam_s) dt_s]
             //   s in t's 16-block      : exp(Lam_t - Lam_s) dt_s for s <= t (exponent
@@ -778,6 +791,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
     // it leaves ls unchanged, so every iteration stages without a branch
     // (which lets the compiler interleave the staging with the update).
     load_tile<kH>(pf, io, tseg0, tseg1, tid);
+    prep_dt<kH, kSp>(pf, tseg0, tseg1, dtb, l);
     TileMode mnext = stage_tile<kH, kSp>(sm, pf, 0, tseg0, tseg1, Ah2, dtb, ls, lsum, tid);
     int slot = 0;
     for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
