@@ -476,14 +476,42 @@ __device__ __forceinline__ void state_update(f32x4 (&Z)[8][2], const unsigned ch
     }
 }
 
-// Registers -> LDS for one tile, and the tile's decay tables: each wave scans
-// a_t = dt_t A_h over its 64 tokens (lane = token), in log2 units.  Updates ls
-// (and lsum, the segment's total log2 decay) and returns how the tile treats
-// the state.
-template <int kH, bool kSp>
-__device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &pf,
-                                               int slot, int64_t t0, int64_t L, float Ah2,
-                                               float dtb, float &ls, float &lsum, int tid)
+// A tile's decay tables, formed in registers from its step sizes (lane =
+// token) before they are staged: each wave scans a_t = dt_t A_h over its 64
+// tokens, in log2 units.  Updates ls (and lsum, the segment's total log2
+// decay) and returns how the tile treats the state.  No other use of ls comes
+// between this and the tile, so the tables of tile k + 1 can be formed while
+// tile k is computed.
+struct Tables {
+    float lam, dtv, vt, wd;
+    TileMode md;
+};
+__device__ __forceinline__ Tables tile_tables(float dtl, int64_t t0, int64_t L, float Ah2, float &ls,
+                                              float &lsum, int l)
+{
+    Tables tb;
+    const float lam = wave_inclusive_sum(dtl * Ah2, l);
+    // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
+    // hold the same sum only up to the summation order, which matters when
+    // the decay is extreme and Lam is large)
+    const int last = (int)((L - t0 < kT) ? (L - t0 > 0 ? L - t0 : 1) : kT) - 1;
+    const float lam_end = lane_f(lam, last);
+    float bias;
+    tb.md = tile_mode(lam_end, ls, lsum, bias);
+    tb.wd = fast_exp2(bias - lam) * dtl;
+    const float q0 = lane_f(lam, 15), q1 = lane_f(lam, 31), q2 = lane_f(lam, 47);
+    const int row = l >> 4;
+    const float lq = row == 0 ? q0 : row == 1 ? q1 : row == 2 ? q2 : lam_end;
+    tb.lam = lam;
+    tb.dtv = dtl;
+    tb.vt = fast_exp2(lq - lam) * dtl;
+    return tb;
+}
+
+// Registers -> LDS for one tile: B, C, this head's x, and the wave's tables.
+template <int kH>
+__device__ __forceinline__ void stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &pf, int slot,
+                                           const Tables &tb, int tid)
 {
     constexpr int kPer = Geom<kH>::kBPer, kRows = Geom<kH>::kThreads / 16;
     const int w = wave_id(), l = tid & 63, pt = tid & 127;
@@ -500,25 +528,10 @@ __device__ __forceinline__ TileMode stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &p
         *reinterpret_cast<uint4 *>(sm.Xt[slot][w >> 1] + row * kXRow +
                                    (((pt & 7) ^ xswz(row)) << 4)) = pf.x[r];
     }
-    // (with the fused step-size prep, pf.dt already holds softplus(u + bias),
-    // formed by prep_dt while the previous tile was computed)
-    const float dtl = pf.dt;
-    const float lam = wave_inclusive_sum(dtl * Ah2, l);
-    // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
-    // hold the same sum only up to the summation order, which matters when
-    // the decay is extreme and Lam is large)
-    const int last = (int)((L - t0 < kT) ? (L - t0 > 0 ? L - t0 : 1) : kT) - 1;
-    const float lam_end = lane_f(lam, last);
-    float bias;
-    const TileMode md = tile_mode(lam_end, ls, lsum, bias);
-    sm.wd[w][l] = fast_exp2(bias - lam) * dtl;
-    const float q0 = lane_f(lam, 15), q1 = lane_f(lam, 31), q2 = lane_f(lam, 47);
-    const int row = l >> 4;
-    const float lq = row == 0 ? q0 : row == 1 ? q1 : row == 2 ? q2 : lam_end;
-    sm.lam[w][l] = lam;
-    sm.dtv[w][l] = dtl;
-    sm.vt[w][l] = fast_exp2(lq - lam) * dtl;
-    return md;
+    sm.wd[w][l] = tb.wd;
+    sm.lam[w][l] = tb.lam;
+    sm.dtv[w][l] = tb.dtv;
+    sm.vt[w][l] = tb.vt;
 }
 
 // The fused step-size prep on a prefetched tile at t0 (lane = token): the
@@ -628,6 +641,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
 
     // y of the tile at t0 from the state entering it, then the state update.
     Prefetch<kH> pf;
+    Tables tnext;
     auto compute_tile = [&](int slot, const TileMode &md, int64_t t0) {
         const unsigned char *Xs = sm.Xt[slot][hs];
         const unsigned char *Bs = sm.Bt[slot];
@@ -685,8 +699,10 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                     Y[q][tb] *= dec;
             }
             lds_barrier();                            // every block of the tile is in Gs
-            // the next tile's step sizes, well before they are staged
+            // the next tile's step sizes and decay tables, well before they
+            // are staged at the end of this tile
             prep_dt<kH, kSp>(pf, t0 + kT, tseg1, dtb, l);
+            tnext = tile_tables(pf.dt, t0 + kT, tseg1, Ah2, ls, lsum, l);
             // Mask and decay, B-operand over tokens s (slot 4 h + i <-> s = 32 jj + 16 h + 4 g + i):
             //   s in an earlier 16-block: exp(Lam_t - Lam_q) * [exp(Lam_q - Lam_s) dt_s]
             //   s in t's 16-block      : exp(Lam_t - Lam_s) dt_s for s <= t (exponent
@@ -792,17 +808,18 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
     // (which lets the compiler interleave the staging with the update).
     load_tile<kH>(pf, io, tseg0, tseg1, tid);
     prep_dt<kH, kSp>(pf, tseg0, tseg1, dtb, l);
-    TileMode mnext = stage_tile<kH, kSp>(sm, pf, 0, tseg0, tseg1, Ah2, dtb, ls, lsum, tid);
+    tnext = tile_tables(pf.dt, tseg0, tseg1, Ah2, ls, lsum, l);
+    stage_tile<kH>(sm, pf, 0, tnext, tid);
     int slot = 0;
     for (int64_t t0 = tseg0; t0 < tseg1; t0 += kT) {
         lds_barrier();
-        const TileMode md = mnext;
+        const TileMode md = tnext.md;
         renorm(md);
         // next tile (nothing past the end); x follows mid-tile
         load_tile<kH, 1>(pf, io, t0 + kT, tseg1, tid);
         compute_tile(slot, md, t0);
         slot ^= 1;
-        mnext = stage_tile<kH, kSp>(sm, pf, slot, t0 + kT, tseg1, Ah2, dtb, ls, lsum, tid);
+        stage_tile<kH>(sm, pf, slot, tnext, tid);
     }
 
     if (!active || seg != a.nseg - 1)
