@@ -432,24 +432,17 @@ __device__ __forceinline__ TileMode tile_mode(float lam_end, float &ls, float &l
 // the tile's weights wd (64 floats, token-indexed).  The B^T operands are read
 // kAhead blocks ahead of their MFMAs, so that their LDS latency overlaps the
 // x scaling and the previous blocks' MFMAs.
-template <int kAhead>
-__device__ __forceinline__ void state_update(f32x4 (&Z)[8][2], const unsigned char *Bs,
-                                             const bf16x8 (&XT)[2][2], const float *wd,
-                                             const TileMode &md, int g, int c)
+// The B operand of the state update: x^T scaled by the tile's weights wd
+// (64 floats, token-indexed; K-slot 4 h + i <-> token 32 jj + 16 h + 4 g + i).
+__device__ __forceinline__ void scale_x(bf16x8 (&XS)[2][2], const bf16x8 (&XT)[2][2],
+                                        const float *wd, int g)
 {
-    bf16x8 BT[8][2];
-#pragma unroll
-    for (int nb = 0; nb < kAhead; ++nb) {
-        BT[nb][0] = tr_operand_b(Bs, 0, 16 * nb, g, c);
-        BT[nb][1] = tr_operand_b(Bs, 1, 16 * nb, g, c);
-    }
     f32x4 wv[2][2];
 #pragma unroll
     for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
             wv[jj][hh] = *reinterpret_cast<const f32x4 *>(&wd[32 * jj + 16 * hh + 4 * g]);
-    bf16x8 XS[2][2];
 #pragma unroll
     for (int q = 0; q < 2; ++q)
 #pragma unroll
@@ -457,6 +450,24 @@ __device__ __forceinline__ void state_update(f32x4 (&Z)[8][2], const unsigned ch
 #pragma unroll
             for (int e = 0; e < 8; ++e)
                 XS[q][jj][e] = (__bf16)((float)XT[q][jj][e] * wv[jj][e >> 2][e & 3]);
+}
+
+// Z <- zscale Z + B^T (wd x) over one tile, with Z[nb][q][i] the state rows
+// n = 16 nb + 4 g + i, column p = 32 ph + 16 q + c (lane (c, g)) of this
+// wave's P half.  A = B^T (rows n) from the swizzled B tile, B = XS (scale_x).
+// The B^T operands are read kAhead blocks ahead of their MFMAs, so that their
+// LDS latency overlaps the previous blocks' MFMAs.
+template <int kAhead>
+__device__ __forceinline__ void state_update(f32x4 (&Z)[8][2], const unsigned char *Bs,
+                                             const bf16x8 (&XS)[2][2], const TileMode &md,
+                                             int g, int c)
+{
+    bf16x8 BT[8][2];
+#pragma unroll
+    for (int nb = 0; nb < kAhead; ++nb) {
+        BT[nb][0] = tr_operand_b(Bs, 0, 16 * nb, g, c);
+        BT[nb][1] = tr_operand_b(Bs, 1, 16 * nb, g, c);
+    }
     if (uniform(md.direct)) {
 #pragma unroll
         for (int nb = 0; nb < 8; ++nb)
@@ -635,8 +646,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
 
     // R <- zscale R + B^T (w dt x); the prefetched tile is live here, so the
     // B^T operands are read half a tile ahead
-    auto update_state = [&](const unsigned char *Bs, const bf16x8 (&XT)[2][2], const TileMode &md) {
-        state_update<4>(Z, Bs, XT, sm.wd[w], md, g, c);
+    auto update_state = [&](const unsigned char *Bs, const bf16x8 (&XS)[2][2], const TileMode &md) {
+        state_update<4>(Z, Bs, XS, md, g, c);
     };
 
     // y of the tile at t0 from the state entering it, then the state update.
@@ -781,7 +792,9 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                 __builtin_amdgcn_raw_buffer_store_b128(v, ry, ylane + 32u * tb * (unsigned)ystride, 0, 0);
             }
         }
-        update_state(Bs, XT, md);
+        bf16x8 XS[2][2];
+        scale_x(XS, XT, sm.wd[w], g);
+        update_state(Bs, XS, md);
     };
 
     // Tile k is staged in ring slot k & 1 (B, C, x) and in the wave's own
@@ -1053,13 +1066,14 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
                     Z[nb][q] *= md.rscale;
         }
         swd[w][l] = fast_exp2(bias - lam) * dtc;
-        bf16x8 XT[2][2];
+        bf16x8 XT[2][2], XS[2][2];
 #pragma unroll
         for (int q = 0; q < 2; ++q)
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj)
                 XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
-        state_update<8>(Z, Bs, XT, swd[w], md, g, c);
+        scale_x(XS, XT, swd[w], g);
+        state_update<8>(Z, Bs, XS, md, g, c);
     };
     // the ring's slots: c = tile t0, m = tile t0 + kT (in flight), f = free
     unsigned cB = aB0, cX = aX0, cD = aD0, mB = aB1, mX = aX1, mD = aD1, fB = aB2, fX = aX2, fD = aD2;
