@@ -23,7 +23,7 @@ the sustained rate.
 Prints ONE JSON line.  ``roofline`` is the dominant prefill kernel
 (chunk_scan_kernel): algorithmic bytes of the layer per launch / its average
 launch time measured with HIP events on the launch stream; ``roofline_step``
-the same bytes over the summed times of every kernel of the step;
+the same bytes over the event-timed whole step;
 ``decode.roofline`` likewise for decode_rows_kernel.  ``traffic`` comes from
 committed rocprofv3 FETCH_SIZE / WRITE_SIZE counters (profiles/counters.json)
 when they were taken on the current kernel sources, else null; so does the
@@ -201,6 +201,45 @@ def write_counters(wname, fetch_csv, write_csv, mops_csv):
     print(json.dumps({wname: kernels}, indent=1))
 
 
+def trace_runs(trace_csv):
+    """Per-dispatch rows of a rocprofv3 kernel trace, grouped into blocks of
+    consecutive dispatches in dispatch order: one kernel with one grid, or the
+    two prefill kernels (state and scan kernel, each with one grid) of the
+    same steps.  Returns [(kernel, grid, count, mean_us, later_half_mean_us,
+    min_us, max_us)] for every kernel of every block."""
+    import csv
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Dispatch_Id"]))
+    pair = ("seg_state_kernel", "chunk_scan_kernel")
+    blocks = []          # [{(kernel, grid): [us, ...]}]
+    for r in rows:
+        name = r["Kernel_Name"]
+        short = next((k for k in KERNELS + ("seg_state_multi_kernel", "chunk_scan_multi_kernel")
+                      if k in name), name.split("(")[0][:40])
+        if "<true>" in name or "ILb1E" in name:
+            short += "<softplus>"
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        us = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        key = (short, grid)
+        cur = blocks[-1] if blocks else None
+        joins = False
+        if cur is not None:
+            if key in cur:
+                joins = True
+            elif len(cur) == 1 and short.split("<")[0] in pair:
+                (k0, _), = cur.keys()
+                joins = k0.split("<")[0] in pair and k0.split("<")[0] != short.split("<")[0]
+        if joins:
+            cur.setdefault(key, []).append(us)
+        else:
+            blocks.append({key: [us]})
+    out = []
+    for b in blocks:
+        for (k, g), v in b.items():
+            half = v[len(v) // 2:]
+            out.append((k, g, len(v), sum(v) / len(v), sum(half) / len(half), min(v), max(v)))
+    return out
+
+
 def to_dev(a, bf16=False):
     import torch
     if bf16:
@@ -276,9 +315,12 @@ def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
     ms = wall * 1e3 / steps
 
     # per-kernel device times: HIP events recorded around each launch on the
-    # stream the kernels run on
+    # stream the kernels run on.  An untimed step is queued ahead of each timed
+    # one, so that the first kernel's start event is not taken on an idle GPU
+    # (the timed entry point synchronises at its end).
     per = {}
     for _ in range(max(3, min(steps, 10))):
+        step()
         _, _, times = ssd.ssd_chunk_scan_timed(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs,
                                                workspace=ws)
         for name, t in times:
@@ -310,13 +352,13 @@ def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
     mfma_counted = None
     if all(v is not None for v in counted.values()):
         cf = sum(counted.values())
-        mfma_counted = {"flop_per_step": cf, "achieved_tflops": cf / (step_k * 1e-3) / 1e12,
-                        "frac": cf / (step_k * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+        mfma_counted = {"flop_per_step": cf, "achieved_tflops": cf / (ev_ms * 1e-3) / 1e12,
+                        "frac": cf / (ev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
                         "per_kernel": {k: {"flop": v,
                                            "frac": v / (kern[k] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS}
                                        for k, v in counted.items()},
                         "source": "profiles/counters.json (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512 "
-                                  "per launch) over the live kernel times"}
+                                  "per launch)"}
     res = {
         "w": w, "ms": ms, "ev_ms": ev_ms, "tokens_per_s": tokens / (ms * 1e-3),
         "kernels_ms": kern, "bytes": nbytes, "flops": flops,
@@ -329,21 +371,23 @@ def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
         },
         "roofline_step": {
             "bound": "hbm", "kernels": sorted(kern),
-            "achieved": nbytes / (step_k * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": nbytes / (step_k * 1e-3) / 1e9 / HBM_PEAK_GBS,
-            "bytes_per_step": nbytes, "kernel_ms_per_step": step_k,
+            "achieved": nbytes / (ev_ms * 1e-3) / 1e9, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": nbytes / (ev_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "bytes_per_step": nbytes, "event_ms_per_step": ev_ms,
+            "kernel_ms_per_step": step_k,
             "traffic": step_traffic(sorted(kern), wname),
-            "note": "the layer's algorithmic bytes over the summed HIP-event times of every "
-                    "kernel of the step",
+            "note": "the layer's algorithmic bytes over the HIP-event time of a whole step "
+                    "(the timed steps back to back); kernel_ms_per_step sums the per-kernel "
+                    "events",
         },
         "mfma": {
             "useful_gflop_per_step": flops / 1e9,
-            "achieved_tflops": flops / (step_k * 1e-3) / 1e12, "peak_tflops": BF16_PEAK_TFLOPS,
-            "frac": flops / (step_k * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "achieved_tflops": flops / (ev_ms * 1e-3) / 1e12, "peak_tflops": BF16_PEAK_TFLOPS,
+            "frac": flops / (ev_ms * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "counted": mfma_counted,
-            "note": "useful (causal-triangle) FLOPs of the whole scan over the summed kernel "
-                    "times; `counted`: the MFMA FLOPs rocprofv3 counts per launch (committed) "
-                    "over the same live times",
+            "note": "useful (causal-triangle) FLOPs of the whole scan over the event-timed "
+                    "step; `counted`: the MFMA FLOPs rocprofv3 counts per launch (committed) "
+                    "over the same live step time, and per kernel over its own event time",
         },
         "path_gbs": nbytes / (ms * 1e-3) / 1e9,
         "dt_softplus_event_ms_per_step": sp_ms,
@@ -882,11 +926,21 @@ def main():
                          "and trace runs: every dispatch of a kernel is then the main workload's)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run one plain 1 GiB device copy (scales the HBM byte counters)")
+    ap.add_argument("--trace-summary", metavar="KERNEL_TRACE_CSV",
+                    help="host only: print the runs of consecutive dispatches of one kernel and "
+                         "grid in a rocprofv3 kernel trace (count, mean, later-half mean) and exit")
     ap.add_argument("--write-counters", nargs=4, metavar=("WORKLOAD", "FETCH_CSV", "WRITE_CSV", "MOPS_CSV"),
                     help="host only: merge three rocprofv3 counter_collection.csv files "
                          "(FETCH_SIZE, WRITE_SIZE, SQ_INSTS_VALU_MFMA_MOPS_BF16; MOPS_CSV may "
                          "be '-') into profiles/counters.json under WORKLOAD and exit")
     args = ap.parse_args()
+    if args.trace_summary:
+        print("| # | kernel | grid (work-items) | dispatches | mean us | later-half mean us | min us | max us |")
+        print("|---|---|---|---|---|---|---|---|")
+        for i, (k, g, n, m, h, lo, hi) in enumerate(trace_runs(args.trace_summary)):
+            if n >= 3 and not k.startswith("__amd") and not k.startswith("void at::"):
+                print(f"| {i} | {k} | {g} | {n} | {m:.2f} | {h:.2f} | {lo:.2f} | {hi:.2f} |")
+        return
     if args.write_counters:
         wl, f, wr, m = args.write_counters
         write_counters(wl, f, wr, None if m == "-" else m)
@@ -919,19 +973,27 @@ def main():
     # of the metric and the other prefill configurations run next, then the
     # headline prefill's warm-up and timed steps, with no host-side gap (input
     # generation) between the GPU legs.
+    def progress(what):
+        print(f"[bench] {what} done", file=sys.stderr, flush=True)
+
     resident = {v: prefill_setup(v) for v in [args.headline] + secondary}
+    progress("inputs")
     if not args.no_decode:
         wd, dec = bench_decode(args)
         extra.update(decode_line(wd, dec))
+        progress("decode")
         if 256 in args.decode_batches:
             extra["gdn_decode"] = bench_gdn(args)
+            progress("gdn decode")
     configs = {}
     for v in secondary:
         configs[v] = prefill_line(bench_prefill(args, v, resident[v], steps=max(args.steps // 2, 5),
                                                 warmup=max(args.warmup, 5)), v)
         del resident[v]
+        progress(f"prefill {v}")
     pre = bench_prefill(args, args.headline, resident[args.headline],
                         extras=not args.no_extras)
+    progress(f"prefill {args.headline}")
     del resident
     torch.cuda.empty_cache()
     w = pre["w"]
@@ -964,7 +1026,9 @@ def main():
             "note": "the same prefill with dt passed as u and softplus(u + dt_bias) formed "
                     "inside the scan kernels (ssd_dims.flags = SSD_DT_SOFTPLUS)"}
         line["prefill_varlen"] = bench_varlen(args)
+        progress("varlen prefill")
         line["noncached_vs_cached"] = bench_noncached(args)
+        progress("non-cached sweep")
     line.update(extra)
     if not args.no_cpu_baseline:
         if "gdn_decode" in line:
