@@ -21,8 +21,11 @@ to pass u instead of dt; the step size is then softplus(u + dt_bias) in the kern
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
+
+import torch
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIBRARY = os.path.join(PKG, "libssd.so")
@@ -115,17 +118,29 @@ def _check(fn: str, rc: int):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """A tensor's device address as an int (ctypes passes it as void*), or NULL."""
+    return None if t is None else t.data_ptr()
 
 
-def _stream(stream):
-    import torch
-    s = torch.cuda.current_stream() if stream is None else stream
-    return ctypes.c_void_p(s.cuda_stream)
+def _current_raw_stream(di):
+    """The current stream's handle on device `di`, without building a Stream object."""
+    get = getattr(torch._C, "_cuda_getCurrentRawStream", None)
+    return get(di) if get is not None else torch.cuda.current_stream(di).cuda_stream
+
+
+def _stream(stream, di):
+    """hipStream_t of `stream`, or of device `di`'s current stream."""
+    return _current_raw_stream(di) if stream is None else stream.cuda_stream
+
+
+def _on(stream):
+    """Allocation context of a call: the caller's stream when one is given (the
+    current stream is the allocator's default otherwise), so that blocks
+    allocated for the call are not handed to other work while its kernels run."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
 
 
 def _io_dtype(t):
-    import torch
     if t.dtype == torch.bfloat16:
         return SSD_BF16
     if t.dtype == torch.float32:
@@ -133,44 +148,43 @@ def _io_dtype(t):
     raise TypeError(f"x/B/C must be bfloat16 or float32, got {t.dtype}")
 
 
-def _need(name, t, dev, dtype=None, shape=None, optional=False):
+def _need(name, t, di, dtype=None, shape=None, optional=False):
     """Checks that a tensor argument can be handed to the kernels as a plain
-    device pointer: a contiguous tensor on `dev` of the stated dtype and shape.
-    A host tensor would hand a host address to a kernel, and a strided view or a
-    wrong dtype would be read as something else, so each raises here instead."""
-    import torch
+    device pointer: a contiguous tensor on GPU `di` of the stated dtype and
+    shape.  A host tensor would hand a host address to a kernel, and a strided
+    view or a wrong dtype would be read as something else, so each raises here
+    instead.  (One combined test on the common path: small decode calls are
+    bound by host time.)"""
     if t is None:
         if optional:
             return
         raise ValueError(f"{name} is required")
-    if not isinstance(t, torch.Tensor):
-        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
-    if t.device != dev:
-        raise ValueError(f"{name} is on {t.device}, expected {dev}")
-    if not t.is_contiguous():
-        raise ValueError(f"{name} must be contiguous")
-    if dtype is not None and t.dtype != dtype:
-        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
-    if shape is not None and tuple(t.shape) != tuple(shape):
+    try:
+        ok = (t.get_device() == di and (dtype is None or t.dtype == dtype) and t.is_contiguous()
+              and (shape is None or t.shape == shape))
+    except AttributeError:
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}") from None
+    if not ok:
+        if t.get_device() != di:
+            raise ValueError(f"{name} is on {t.device}, expected cuda:{di}")
+        if dtype is not None and t.dtype != dtype:
+            raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
         raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
 
 
 def _device_of(t):
-    """The device of the first tensor argument, which must be a GPU tensor."""
-    if t.device.type != "cuda":
+    """The device index of the first tensor argument, which must be a GPU tensor."""
+    di = t.get_device()
+    if di < 0:
         raise ValueError(f"arguments must be device (HIP) tensors, got one on {t.device}")
-    return t.device
+    return di
 
 
-def _stream_obj(stream, dev):
-    import torch
-    return torch.cuda.current_stream(dev) if stream is None else stream
-
-
-def _bias_check(dev, H, dt_softplus, dt_bias):
-    import torch
+def _bias_check(di, H, dt_softplus, dt_bias):
     if dt_softplus:
-        _need("dt_bias", dt_bias, dev, torch.float32, (H,), optional=True)
+        _need("dt_bias", dt_bias, di, torch.float32, (H,), optional=True)
 
 
 def make_dims(batch, seqlen, nheads, headdim, dstate, ngroups, chunk, io_dtype,
@@ -193,7 +207,6 @@ def ssd_chunk_scan_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroup
 
 def ssd_state_init(state, src=None, stream=None):
     """state [B, H, P, N] fp32 <- src (or zeros)."""
-    import torch
     dev = _device_of(state)
     _need("state", state, dev, torch.float32)
     if state.dim() != 4:
@@ -202,13 +215,12 @@ def ssd_state_init(state, src=None, stream=None):
     _need("src", src, dev, torch.float32, state.shape, optional=True)
     d = make_dims(b, 0, h, p, n, 1, 1, SSD_F32)
     _check("ssd_state_init", load().ssd_state_init(ctypes.byref(d), _ptr(state), _ptr(src),
-                                                   _stream(stream)))
+                                                   _stream(stream, dev)))
     return state
 
 
 def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspace,
                dt_softplus=False, dt_bias=None, stream=None, need_workspace=True):
-    import torch
     dev = _device_of(x)
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be [B, L, H, P] and B, C [B, L, G, N]")
@@ -231,7 +243,7 @@ def _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, workspac
     need = ssd_chunk_scan_workspace_size(bsz, L, H, P, N, G, chunk, io) if need_workspace else 0
     # outputs and workspace come from the allocator on the call's own stream, so
     # that their blocks are not handed to other work while the kernels run
-    with torch.cuda.stream(_stream_obj(stream, dev)):
+    with _on(stream):
         if y is None:
             y = torch.empty_like(x)
         if final_state is None:
@@ -249,7 +261,7 @@ def ssd_chunk_scan(x, dt, A, B, C, D, chunk, initial_state=None, y=None, final_s
     """Prefill over x[B, L, H, P]; returns (y, final_state)."""
     args, y, fs, ws = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state,
                                  workspace, dt_softplus, dt_bias, stream)
-    _check("ssd_chunk_scan", load().ssd_chunk_scan(*args, _stream(stream)))
+    _check("ssd_chunk_scan", load().ssd_chunk_scan(*args, _stream(stream, x.get_device())))
     return y, fs
 
 
@@ -261,7 +273,8 @@ def ssd_chunk_scan_noalloc(x, dt, A, B, C, D, chunk, initial_state=None, y=None,
     race on the scratch array.  Returns (y, final_state)."""
     args, y, fs, _ = _scan_args(x, dt, A, B, C, D, chunk, initial_state, y, final_state, None,
                                 dt_softplus, dt_bias, stream, need_workspace=False)
-    _check("ssd_chunk_scan_noalloc", load().ssd_chunk_scan_noalloc(*args[:10], _stream(stream)))
+    _check("ssd_chunk_scan_noalloc",
+           load().ssd_chunk_scan_noalloc(*args[:10], _stream(stream, x.get_device())))
     return y, fs
 
 
@@ -274,15 +287,14 @@ def ssd_chunk_scan_timed(x, dt, A, B, C, D, chunk, initial_state=None, y=None, f
     ms = (ctypes.c_float * cap)()
     names = (ctypes.c_char_p * cap)()
     n = ctypes.c_int(cap)
-    _check("ssd_chunk_scan_timed", load().ssd_chunk_scan_timed(*args, _stream(stream), ms, names,
-                                                               ctypes.byref(n)))
+    _check("ssd_chunk_scan_timed", load().ssd_chunk_scan_timed(
+        *args, _stream(stream, x.get_device()), ms, names, ctypes.byref(n)))
     return y, fs, [(names[i].decode(), float(ms[i])) for i in range(n.value)]
 
 
 def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=False,
                     dt_bias=None):
     """One decode step: x[B, H, P], B/C[B, G, N], state[B, H, P, N] updated in place; returns y."""
-    import torch
     dev = _device_of(x)
     if x.dim() != 3 or B.dim() != 3:
         raise ValueError("x must be [B, H, P] and B, C [B, G, N]")
@@ -300,11 +312,11 @@ def ssd_decode_step(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=F
     _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x), dt_softplus, dt_bias)
     if y is None:
-        with torch.cuda.stream(_stream_obj(stream, dev)):
+        with _on(stream):
             y = torch.empty_like(x)
     _check("ssd_decode_step", load().ssd_decode_step(
         ctypes.byref(d), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(state),
-        _ptr(y), _stream(stream)))
+        _ptr(y), _stream(stream, dev)))
     return y
 
 
@@ -312,7 +324,6 @@ def ssd_decode_steps(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=
                      dt_bias=None):
     """S decode steps in one launch: x[S, B, H, P], dt[S, B, H], B/C[S, B, G, N];
     state[B, H, P, N] updated in place (read and written once); returns y[S, B, H, P]."""
-    import torch
     dev = _device_of(x)
     if x.dim() != 4 or B.dim() != 4:
         raise ValueError("x must be [S, B, H, P] and B, C [S, B, G, N]")
@@ -330,11 +341,11 @@ def ssd_decode_steps(x, dt, A, B, C, D, state, y=None, stream=None, dt_softplus=
     _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(bsz, 1, H, P, N, G, 1, _io_dtype(x), dt_softplus, dt_bias)
     if y is None:
-        with torch.cuda.stream(_stream_obj(stream, dev)):
+        with _on(stream):
             y = torch.empty_like(x)
     _check("ssd_decode_steps", load().ssd_decode_steps(
         ctypes.byref(d), ctypes.c_int64(nsteps), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-        _ptr(D), _ptr(state), _ptr(y), _stream(stream)))
+        _ptr(D), _ptr(state), _ptr(y), _stream(stream, dev)))
     return y
 
 
@@ -360,7 +371,6 @@ def ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, initial_states=N
     """Prefill of a packed batch: x[T, H, P], dt[T, H], B/C[T, G, N]; sequence i is
     tokens cu_seqlens[i] .. cu_seqlens[i+1]-1 (a host sequence of S + 1 offsets).
     Returns (y[T, H, P], final_states[S, H, P, N])."""
-    import torch
     dev = _device_of(x)
     if x.dim() != 3 or B.dim() != 3:
         raise ValueError("x must be [T, H, P] and B, C [T, G, N]")
@@ -383,7 +393,7 @@ def ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, initial_states=N
     _bias_check(dev, H, dt_softplus, dt_bias)
     d = make_dims(nseq, T, H, P, N, G, chunk, io, dt_softplus, dt_bias)
     need = ssd_chunk_scan_varlen_workspace_size(cu, H, P, N, G, chunk, io)
-    with torch.cuda.stream(_stream_obj(stream, dev)):
+    with _on(stream):
         if y is None:
             y = torch.empty_like(x)
         if final_states is None:
@@ -394,14 +404,13 @@ def ssd_chunk_scan_varlen(x, dt, A, B, C, D, cu_seqlens, chunk, initial_states=N
     _check("ssd_chunk_scan_varlen", load().ssd_chunk_scan_varlen(
         ctypes.byref(d), cup, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
         _ptr(initial_states), _ptr(y), _ptr(final_states), _ptr(workspace), ws_bytes,
-        _stream(stream)))
+        _stream(stream, dev)))
     return y, final_states
 
 
 def ssd_gdn_decode_step(q, k, v, g, beta, state, o=None, stream=None):
     """One Gated DeltaNet decode step: q, k [B, Hk, dk], v [B, Hv, dv], g, beta [B, Hv]
     fp32, state [B, Hv, dk, dv] fp32 updated in place; returns o [B, Hv, dv]."""
-    import torch
     dev = _device_of(q)
     if q.dim() != 3 or v.dim() != 3:
         raise ValueError("q, k must be [B, Hk, dk] and v [B, Hv, dv]")
@@ -417,18 +426,17 @@ def ssd_gdn_decode_step(q, k, v, g, beta, state, o=None, stream=None):
     _need("o", o, dev, q.dtype, v.shape, optional=True)
     d = SsdGdnDims(bsz, Hk, Hv, dk, dv, _io_dtype(q), 0)
     if o is None:
-        with torch.cuda.stream(_stream_obj(stream, dev)):
+        with _on(stream):
             o = torch.empty_like(v)
     _check("ssd_gdn_decode_step", load().ssd_gdn_decode_step(
         ctypes.byref(d), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state), _ptr(o),
-        _stream(stream)))
+        _stream(stream, dev)))
     return o
 
 
 def ssd_gdn_decode_steps(q, k, v, g, beta, state, o=None, stream=None):
     """S Gated DeltaNet steps in one launch: q, k [S, B, Hk, dk], v [S, B, Hv, dv],
     g, beta [S, B, Hv]; state [B, Hv, dk, dv] read and written once; returns o [S, B, Hv, dv]."""
-    import torch
     dev = _device_of(q)
     if q.dim() != 4 or v.dim() != 4:
         raise ValueError("q, k must be [S, B, Hk, dk] and v [S, B, Hv, dv]")
@@ -444,9 +452,9 @@ def ssd_gdn_decode_steps(q, k, v, g, beta, state, o=None, stream=None):
     _need("o", o, dev, q.dtype, v.shape, optional=True)
     d = SsdGdnDims(bsz, Hk, Hv, dk, dv, _io_dtype(q), 0)
     if o is None:
-        with torch.cuda.stream(_stream_obj(stream, dev)):
+        with _on(stream):
             o = torch.empty_like(v)
     _check("ssd_gdn_decode_steps", load().ssd_gdn_decode_steps(
         ctypes.byref(d), ctypes.c_int64(nsteps), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-        _ptr(state), _ptr(o), _stream(stream)))
+        _ptr(state), _ptr(o), _stream(stream, dev)))
     return o
