@@ -48,6 +48,12 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 FP32_VALU_PEAK_TFLOPS = 157.3  # MI355X fp32 vector, TFLOP/s (256 CU x 2.4 GHz x 256 FLOP/clk)
+# The same without packed fp32 (one FMA per lane and instruction: 4 SIMDs x 16
+# lanes x 2 FLOP per clock and CU), the ceiling of kernels built without
+# packed fp32 instructions, as libssd is
+FP32_UNPACKED_PEAK_TFLOPS = 78.6
+UNPACKED_NOTE = ("frac_unpacked: against 78.6 TFLOP/s, the fp32 vector rate without packed fp32 "
+                 "instructions (libssd is built without them)")
 METRIC = "SSD prefill tokens/s (MFMA %) + decode steps/s (HBM GB/s %) at 2.7B-layer shape"
 CSRC = "state_space_model_mamba_amd/csrc/"
 # the source of each measured kernel; its counters in profiles/counters.json are
@@ -587,6 +593,8 @@ def bench_gdn(args):
                 "bound": "alu", "kernel": "gdn_steps_kernel", "batch": 256,
                 "achieved": r["steps_launch_tflops"], "peak": FP32_VALU_PEAK_TFLOPS,
                 "unit": "TFLOP/s", "frac": r["steps_launch_tflops"] / FP32_VALU_PEAK_TFLOPS,
+                "frac_unpacked": r["steps_launch_tflops"] / FP32_UNPACKED_PEAK_TFLOPS,
+                "note": UNPACKED_NOTE,
                 "flops_per_step": gdn_flops(256, sh),
                 "avg_launch_ms": r["steps_launch_ms_per_step"] * nsteps},
                 "note": f"the same {nsteps} steps as one ssd_gdn_decode_steps launch, the state read and "
@@ -910,6 +918,8 @@ def decode_line(wd, dec):
                      "achieved": fl / (m_ms * 1e-3) / 1e12, "peak": FP32_VALU_PEAK_TFLOPS,
                      "unit": "TFLOP/s",
                      "frac": fl / (m_ms * 1e-3) / 1e12 / FP32_VALU_PEAK_TFLOPS,
+                     "frac_unpacked": fl / (m_ms * 1e-3) / 1e12 / FP32_UNPACKED_PEAK_TFLOPS,
+                     "note": UNPACKED_NOTE,
                      "traffic": committed_traffic("decode_steps_kernel"),
                      "flops_per_step": fl, "avg_launch_ms": m_ms * d["steps"]},
         "batches": {str(b): {"steps_per_s": r["steps_launch_steps_per_s"],
