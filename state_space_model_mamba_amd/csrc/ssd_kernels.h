@@ -31,7 +31,9 @@ hipError_t log_kernel(EventLog *log, const char *name, hipStream_t s);
 // to first order in d.  Dropping the 1 / (1 + e) changes the result by at most
 // |d| e <= 2^-24 e, i.e. 2^-24 of log1p(e) ~ e: no reciprocal, and w = 1
 // (e below 2^-24) needs no branch (d = -e).  The exp and log are the hardware
-// exp2 / log2.  Positions past the end of a sequence keep a step size of 0.
+// exp2 / log2 (log(w) = log2(w) ln 2; w in [1, 2] needs none of the denormal
+// handling of the library log).  Positions past the end of a sequence keep a
+// step size of 0.
 struct DtPrep {
     const float *bias;
     int softplus;
@@ -41,9 +43,9 @@ __device__ __forceinline__ float softplus_dt(float u, float bias)
 {
     const float v = u + bias;
     const float e = __expf(-fabsf(v));   // (0, 1]
-    const float w = 1.f + e;
+    const float w = 1.f + e;             // [1, 2]: no denormal handling needed
     const float d = (w - 1.f) - e;       // the rounding error of 1 + e, exactly
-    return fmaxf(v, 0.f) + (__logf(w) - d);
+    return fmaxf(v, 0.f) + (__builtin_amdgcn_logf(w) * 0.6931471806f - d);
 }
 
 // Sum of a wave value with its partner lane across lane bit 4 or 5 (the lane

@@ -174,6 +174,14 @@ __device__ __forceinline__ float lane_f(float v, int lane)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
+// kNested: the earlier rows' totals as one nested select, which the compiler
+// turns into divergent branches; otherwise as three independent selects (no
+// branch).  Each row adds the same terms in the same order either way.  The
+// state kernel takes the selects (1.5-2.5 us faster); the scan kernel keeps the
+// nested form, which measured 2-5 us faster there in its tables of the next
+// tile (formed mid-tile, where the branches also bound how far the scheduler
+// moves that chain).
+template <bool kNested = false>
 __device__ __forceinline__ float wave_inclusive_sum(float v, int lane)
 {
     v += dpp_row_shr<0x111>(v);   // row_shr:1
@@ -182,7 +190,10 @@ __device__ __forceinline__ float wave_inclusive_sum(float v, int lane)
     v += dpp_row_shr<0x118>(v);   // row_shr:8
     const float r0 = lane_f(v, 15), r1 = lane_f(v, 31), r2 = lane_f(v, 47);
     const int row = lane >> 4;
-    return v + (row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+    if constexpr (kNested)
+        return v + (row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
+    else
+        return v + (((row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f)) + (row >= 3 ? r2 : 0.f));
 }
 
 // K-major MFMA operand from a token-major LDS tile with gfx950's transpose read
@@ -401,28 +412,21 @@ struct TileMode {
 // update weights are wd_s = dt_s 2^(bias - lam_s).
 __device__ __forceinline__ TileMode tile_mode(float lam_end, float &ls, float &lsum, float &bias)
 {
+    // (selects rather than branches: the decision ends a dependent chain from
+    // the step sizes, and branches here would split the code that follows
+    // from that chain)
     lsum += lam_end;
     TileMode md;
-    md.renorm = false;
-    md.rscale = 1.f;
-    if (lam_end < -kRenorm) {
-        md.direct = true;
-        md.ly = ls;
-        md.zscale = fast_exp2(ls + lam_end);
-        bias = lam_end;
-        ls = 0.f;
-    } else {
-        if (ls + lam_end < -kRenorm) {
-            md.renorm = true;
-            md.rscale = fast_exp2(ls);
-            ls = 0.f;
-        }
-        md.direct = false;
-        md.ly = ls;
-        md.zscale = 1.f;
-        bias = -ls;
-        ls += lam_end;
-    }
+    const bool direct = lam_end < -kRenorm;
+    const bool renorm = !direct && ls + lam_end < -kRenorm;
+    const float ls_in = renorm ? 0.f : ls;       // ls after a renormalisation
+    md.direct = direct;
+    md.renorm = renorm;
+    md.rscale = renorm ? fast_exp2(ls) : 1.f;
+    md.ly = direct ? ls : ls_in;
+    md.zscale = direct ? fast_exp2(ls + lam_end) : 1.f;
+    bias = direct ? lam_end : -ls_in;
+    ls = direct ? 0.f : ls_in + lam_end;
     return md;
 }
 
@@ -501,11 +505,13 @@ __device__ __forceinline__ Tables tile_tables(float dtl, int64_t t0, int64_t L, 
                                               float &lsum, int l)
 {
     Tables tb;
-    const float lam = wave_inclusive_sum(dtl * Ah2, l);
+    const float lam = wave_inclusive_sum<true>(dtl * Ah2, l);
     // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
     // hold the same sum only up to the summation order, which matters when
     // the decay is extreme and Lam is large)
-    const int last = (int)((L - t0 < kT) ? (L - t0 > 0 ? L - t0 : 1) : kT) - 1;
+    // (a scalar: readlane needs a uniform lane)
+    const int last = __builtin_amdgcn_readfirstlane(
+        (int)std::min<int64_t>(std::max<int64_t>(L - t0, 1), kT) - 1);
     const float lam_end = lane_f(lam, last);
     float bias;
     tb.md = tile_mode(lam_end, ls, lsum, bias);
@@ -1052,10 +1058,18 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
         st_issue(io, Bn, Xn, Dn, t0 + 2 * kT, tseg1, w);
         const unsigned char *Bs = lds_ptr(aB), *Xs = lds_ptr(aX), *Ds = lds_ptr(aD);
         float dtc = reinterpret_cast<const float *>(Ds)[kStHeads * l + hs];
-        if constexpr (kSp)   // the step size from u; tokens past the end keep 0
-            dtc = l < tseg1 - t0 ? softplus_dt(dtc, dtb) : 0.f;
+        if constexpr (kSp) {
+            // the step size from u, tokens past the end keep 0: formed in
+            // every lane and then selected (as a conditional it became a
+            // divergent branch ahead of the decay scan; 3 us slower)
+            float sp = softplus_dt(dtc, dtb);
+            asm volatile("" : "+v"(sp));
+            dtc = l < tseg1 - t0 ? sp : 0.f;
+        }
         const float lam = wave_inclusive_sum(dtc * Ah2, l);
-        const int last = (int)std::min<int64_t>(std::max<int64_t>(tseg1 - t0, 1), kT) - 1;
+        // (a scalar: readlane needs a uniform lane)
+        const int last = __builtin_amdgcn_readfirstlane(
+            (int)std::min<int64_t>(std::max<int64_t>(tseg1 - t0, 1), kT) - 1);
         float bias;
         const TileMode md = tile_mode(lane_f(lam, last), ls, lsum, bias);
         if (uniform(md.renorm)) {
