@@ -320,6 +320,19 @@ def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
     ev_ms = e0.elapsed_time(e1) / steps
     ms = wall * 1e3 / steps
 
+    # per-kernel device times: HIP events recorded around each launch on the
+    # stream the kernels run on.  An untimed step is queued ahead of each timed
+    # one, so that the first kernel's start event is not taken on an idle GPU
+    # (the timed entry point synchronises at its end).
+    per = {}
+    for _ in range(max(3, min(steps, 10))):
+        step()
+        _, _, times = ssd.ssd_chunk_scan_timed(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs,
+                                               workspace=ws)
+        for name, t in times:
+            per.setdefault(name, []).append(t)
+    kern = {k: float(np.mean(v)) for k, v in per.items()}
+
     sp = None
     if extras:
         # the same step with the fused step-size prep (dt read as u, softplus(u +
@@ -333,6 +346,9 @@ def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
                                dt_softplus=True, dt_bias=bias)
 
         blk, rounds = max(5, min(steps, 20)), 5
+        for _ in range(10):      # the fused code loaded, the clock back up after the syncs above
+            fused()
+            step()
         marks = []
         for _ in range(rounds):
             for fn in (step, fused):
@@ -349,19 +365,6 @@ def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
               "overhead_pct": 100.0 * (sp_ms / plain_ms - 1.0),
               "timing": f"{rounds} alternating pairs of {blk}-step blocks (plain, fused), "
                         "queued back to back; medians of the blocks"}
-
-    # per-kernel device times: HIP events recorded around each launch on the
-    # stream the kernels run on.  An untimed step is queued ahead of each timed
-    # one, so that the first kernel's start event is not taken on an idle GPU
-    # (the timed entry point synchronises at its end).
-    per = {}
-    for _ in range(max(3, min(steps, 10))):
-        step()
-        _, _, times = ssd.ssd_chunk_scan_timed(x, dt, dA, B, C, dD, w.chunk, y=y, final_state=fs,
-                                               workspace=ws)
-        for name, t in times:
-            per.setdefault(name, []).append(t)
-    kern = {k: float(np.mean(v)) for k, v in per.items()}
     nbytes = prefill_bytes(w)
     flops = prefill_useful_flops(w)
     k3 = kern["chunk_scan_kernel"]
