@@ -85,3 +85,43 @@ def test_noalloc_without_workspace_need():
     _, _, _, g = inputs(w)
     y1, s1, y2, s2 = both(w, g)
     assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+
+
+def test_noalloc_in_captured_graph():
+    """The callers the entry point is for: it is captured once into a HIP graph
+    (outputs passed in, no allocation anywhere in the call) and the graph is
+    replayed three times, with new inputs copied into the captured buffers
+    eagerly between replays; every replay must equal an eager ssd_chunk_scan
+    with its own workspace on the same inputs, bit for bit."""
+    w = si.small_workload(batch=2, seqlen=1500, nheads=8, ngroups=2, chunk=128, seed=311)
+    assert ssd.ssd_chunk_scan_workspace_size(w.batch, w.seqlen, w.nheads, 64, 128,
+                                             w.ngroups, w.chunk) > 0
+    sets = []
+    for k in range(3):
+        _, _, _, g = inputs(si.small_workload(batch=2, seqlen=1500, nheads=8, ngroups=2,
+                                              chunk=128, seed=312 + k))
+        sets.append(g)
+    buf = {k: v.clone() for k, v in sets[0].items()}
+    y = torch.empty_like(buf["x"])
+    s = torch.empty((w.batch, w.nheads, 64, 128), device="cuda")
+    args = lambda g: (g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], w.chunk)
+    ssd.ssd_chunk_scan_noalloc(*args(buf), y=y, final_state=s)     # first call: scratch address
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            ssd.ssd_chunk_scan_noalloc(*args(buf), y=y, final_state=s)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep, g in enumerate(sets):
+        for k in buf:
+            buf[k].copy_(g[k])
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        y_ref, s_ref = ssd.ssd_chunk_scan(*args(g))
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), f"replay {rep}: y"
+        assert torch.equal(s, s_ref), f"replay {rep}: final state"
