@@ -1227,13 +1227,19 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, i
     p.chunks_per_seg = std::max<int64_t>(1, (p.nchunks + nseg - 1) / nseg);
     p.nseg = std::max<int64_t>(1, (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg);
     // The state kernel may cut each of its segments into units to fill the
-    // chip (its cost ~ rounds * tiles per unit); every unit adds one more
-    // state to write, and the scan kernel's last segment chains (nseg-1) * nsub
-    // states before its first tile.
+    // chip; every unit adds one more state to write, and the scan kernel's
+    // last segment chains (nseg-1) * nsub states before its first tile.  Cost
+    // in microseconds, from times measured at the 2.7B layer for 1 to 4 units
+    // per segment: the state kernel runs in rounds of `slots1` work-groups; a
+    // tile costs a work-group ~1.9 us when few run, and their HBM traffic
+    // (~49 KB per tile and work-group) caps a round at ~5 TB/s; each chained
+    // unit state adds ~2.75 us to the scan kernel's prologue.
     const int64_t seg_tiles = p.chunks_per_seg * Q / kT;
     p.nsub = 1;
     p.unit_tokens = p.chunks_per_seg * Q;
     if (p.nseg > 1) {
+        constexpr double kTileUs = 1.9, kChainUs = 2.75, kHbmBytesPerUs = 5.0e6;
+        constexpr double kTileBytes = (double)kT * (kStHeads * kP * 2 + kN * 2 + kStHeads * 4);
         int64_t want = use_env ? env_int("SSD_NSUB", 0) : 0;
         double best = 1e300;
         for (int64_t k = 1; k <= 8; ++k) {
@@ -1241,9 +1247,11 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, i
             const int64_t nk = (seg_tiles + ut - 1) / ut;           // non-empty units
             if (nk != k)
                 continue;
-            const double rounds = (double)((per_seg1 * (p.nseg - 1) * nk + slots1 - 1) / slots1);
-            // (a chained state costs the scan kernel's critical path ~ 1 tile)
-            const double cost = rounds * (double)ut + (double)nk + (double)((p.nseg - 1) * nk);
+            const int64_t wgs = per_seg1 * (p.nseg - 1) * nk;
+            const double rounds = (double)((wgs + slots1 - 1) / slots1);
+            const double active = (double)std::min(wgs, slots1);
+            const double tile_us = std::max(kTileUs, active * kTileBytes / kHbmBytesPerUs);
+            const double cost = rounds * (double)ut * tile_us + kChainUs * (double)((p.nseg - 1) * nk);
             if (want > 0 ? k == want : cost < best) {
                 best = cost;
                 p.nsub = nk;
