@@ -491,6 +491,25 @@ __device__ __forceinline__ void state_update(f32x4 (&Z)[8][2], const unsigned ch
     }
 }
 
+// The state update of state_update on B^T operands read beforehand (all of
+// them, so that their LDS latency overlaps whatever comes between).
+__device__ __forceinline__ void state_update_pre(f32x4 (&Z)[8][2], const bf16x8 (&BT)[8][2],
+                                                 const bf16x8 (&XS)[2][2], const TileMode &md)
+{
+    if (uniform(md.direct)) {
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+            for (int q = 0; q < 2; ++q)
+                Z[nb][q] *= md.zscale;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+            Z[nb][q] = mfma32(BT[nb][1], XS[q][1], mfma32(BT[nb][0], XS[q][0], Z[nb][q]));
+}
+
 // A tile's decay tables, formed in registers from its step sizes (lane =
 // token) before they are staged: each wave scans a_t = dt_t A_h over its 64
 // tokens, in log2 units.  Updates ls (and lsum, the segment's total log2
@@ -1058,6 +1077,18 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
         st_issue(io, Bn, Xn, Dn, t0 + 2 * kT, tseg1, w);
         const unsigned char *Bs = lds_ptr(aB), *Xs = lds_ptr(aX), *Ds = lds_ptr(aD);
         float dtc = reinterpret_cast<const float *>(Ds)[kStHeads * l + hs];
+        // the update's operands, read while the decay scan below runs
+        bf16x8 XT[2][2], BT[8][2];
+#pragma unroll
+        for (int q = 0; q < 2; ++q)
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+                XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) {
+            BT[nb][0] = tr_operand_b(Bs, 0, 16 * nb, g, c);
+            BT[nb][1] = tr_operand_b(Bs, 1, 16 * nb, g, c);
+        }
         if constexpr (kSp) {
             // the step size from u, tokens past the end keep 0: formed in
             // every lane and then selected (as a conditional it became a
@@ -1072,6 +1103,9 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
             (int)std::min<int64_t>(std::max<int64_t>(tseg1 - t0, 1), kT) - 1);
         float bias;
         const TileMode md = tile_mode(lane_f(lam, last), ls, lsum, bias);
+        swd[w][l] = fast_exp2(bias - lam) * dtc;
+        bf16x8 XS[2][2];
+        scale_x(XS, XT, swd[w], g);
         if (uniform(md.renorm)) {
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb)
@@ -1079,15 +1113,7 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
                 for (int q = 0; q < 2; ++q)
                     Z[nb][q] *= md.rscale;
         }
-        swd[w][l] = fast_exp2(bias - lam) * dtc;
-        bf16x8 XT[2][2], XS[2][2];
-#pragma unroll
-        for (int q = 0; q < 2; ++q)
-#pragma unroll
-            for (int jj = 0; jj < 2; ++jj)
-                XT[q][jj] = tr_operand_x(Xs, jj, 32 * ph + 16 * q, g, c);
-        scale_x(XS, XT, swd[w], g);
-        state_update<8>(Z, Bs, XS, md, g, c);
+        state_update_pre(Z, BT, XS, md);
     };
     // the ring's slots: c = tile t0, m = tile t0 + kT (in flight), f = free
     unsigned cB = aB0, cX = aX0, cD = aD0, mB = aB1, mX = aX1, mD = aD1, fB = aB2, fX = aX2, fD = aD2;
