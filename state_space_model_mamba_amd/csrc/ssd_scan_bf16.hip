@@ -935,25 +935,55 @@ __device__ __forceinline__ void lds_load4(unsigned dst, u32x4 rsrc, unsigned vof
 }
 #pragma clang diagnostic pop
 
-// Loads of the tile at t0 into one ring slot, bounded by the unit's end (a
-// tile past it reads as zeros): kStLoads instructions per wave.  Lane l of a
-// 1 KB block writes bytes 16 l .. 16 l + 15 of it, so the swizzle of the B
-// and x tiles is applied to the source offsets.
-__device__ __forceinline__ void st_issue(const StIo &io, unsigned Bslot, unsigned Xslot, unsigned Dslot,
-                                         int64_t t0, int64_t tend, int w)
+// The next tile a wave loads: where its rows start, and how many tokens are
+// left from it to the unit's end.  Advanced by one tile per issue, so that a
+// tile's descriptors take a 64-bit add and 32-bit clamps (no 64-bit index
+// arithmetic or compares per tile).
+struct StCursor {
+    uint64_t b, x, d;   // byte addresses of the tile's first row of B, x, dt
+    int rows;           // tokens from the tile to the unit's end (<= 0: past it)
+};
+
+// tile_words on a byte address and a 32-bit row count.
+// (the clamp is written out as scalar min and max: as C, the compiler folds
+// it into a vector median, and the products after it then run on the vector
+// unit too)
+__device__ __forceinline__ u32x4 tile_words32(uint64_t p, int rows, unsigned pitch, unsigned row_bytes)
 {
-    const int64_t rows = tend - t0;
-    const u32x4 rb = tile_words(io.B + t0 * (io.bp / 2), rows, (unsigned)io.bp, kN * 2);
+    int r;
+    asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(rows), "n"(kT));
+    const int bytes = r * (int)pitch - (int)pitch + (int)row_bytes;
+    u32x4 d;
+    d.x = __builtin_amdgcn_readfirstlane((unsigned)p);
+    d.y = __builtin_amdgcn_readfirstlane((unsigned)(p >> 32)) & 0xffffu;
+    d.z = __builtin_amdgcn_readfirstlane((unsigned)(bytes < 0 ? 0 : bytes));
+    d.w = 0x00020000u;
+    return d;
+}
+
+// Loads of the cursor's tile into one ring slot, bounded by the unit's end (a
+// tile past it reads as zeros): kStLoads instructions per wave; then the
+// cursor moves to the next tile.  Lane l of a 1 KB block writes bytes
+// 16 l .. 16 l + 15 of it, so the swizzle of the B and x tiles is applied to
+// the source offsets.
+__device__ __forceinline__ void st_issue(const StIo &io, StCursor &cur, unsigned Bslot, unsigned Xslot,
+                                         unsigned Dslot, int w)
+{
+    const u32x4 rb = tile_words32(cur.b, cur.rows, (unsigned)io.bp, kN * 2);
 #pragma unroll
     for (int k = 0; k < kStBBlocks; ++k)
         lds_load16(Bslot + 1024 * (kStBBlocks * w + k), rb, io.boff[k]);
-    const u32x4 rx = tile_words(io.x + t0 * (io.xp / 2), rows, (unsigned)io.xp, kP * 2);
+    const u32x4 rx = tile_words32(cur.x, cur.rows, (unsigned)io.xp, kP * 2);
 #pragma unroll
     for (int k = 0; k < kStXBlocks; ++k)
         lds_load16(Xslot + 1024 * (kStXBlocks * (w & 1) + k), rx, io.xoff[k]);
-    const u32x4 rd = tile_words(io.dt + t0 * (io.dp / 4), rows, (unsigned)io.dp, io.dbytes);
+    const u32x4 rd = tile_words32(cur.d, cur.rows, (unsigned)io.dp, io.dbytes);
     if ((threadIdx.x & 63) < 32)
         lds_load4(Dslot + 128 * w, rd, io.doff);
+    cur.b += (uint64_t)kT * (uint64_t)io.bp;
+    cur.x += (uint64_t)kT * (uint64_t)io.xp;
+    cur.d += (uint64_t)kT * (uint64_t)io.dp;
+    cur.rows -= kT;
 }
 
 // The LDS location at byte address a, as a pointer.
@@ -1066,15 +1096,20 @@ __device__ __forceinline__ void seg_state_body(const SegArgs &a, int64_t bid, in
     const unsigned aX0 = SSD_LDS(&sX0[hs][0]), aX1 = SSD_LDS(&sX1[hs][0]), aX2 = SSD_LDS(&sX2[hs][0]);
     const unsigned aD0 = SSD_LDS(sD0), aD1 = SSD_LDS(sD1), aD2 = SSD_LDS(sD2);
 #undef SSD_LDS
-    st_issue(io, aB0, aX0, aD0, tseg0, tseg1, w);
-    st_issue(io, aB1, aX1, aD1, tseg0 + kT, tseg1, w);
+    StCursor cur;
+    cur.b = reinterpret_cast<uint64_t>(io.B + tseg0 * (io.bp / 2));
+    cur.x = reinterpret_cast<uint64_t>(io.x + tseg0 * (io.xp / 2));
+    cur.d = reinterpret_cast<uint64_t>(io.dt + tseg0 * (io.dp / 4));
+    cur.rows = (int)std::min<int64_t>(tseg1 - tseg0, int64_t(1) << 30);
+    st_issue(io, cur, aB0, aX0, aD0, w);
+    st_issue(io, cur, aB1, aX1, aD1, w);
 
     // tile t0 in slot (Bs, Xs, Ds); tile t0 + 2 kT goes to (Bn, Xn, Dn)
     auto step = [&](unsigned aB, unsigned aX, unsigned aD, unsigned Bn, unsigned Xn, unsigned Dn,
                     int64_t t0) {
         wait_vmcnt<kStLoads>();                   // this wave's loads of tile t0 are in
         lds_barrier();                            // ... and every wave's; slot of t0 - kT free
-        st_issue(io, Bn, Xn, Dn, t0 + 2 * kT, tseg1, w);
+        st_issue(io, cur, Bn, Xn, Dn, w);      // tile t0 + 2 kT
         const unsigned char *Bs = lds_ptr(aB), *Xs = lds_ptr(aX), *Ds = lds_ptr(aD);
         float dtc = reinterpret_cast<const float *>(Ds)[kStHeads * l + hs];
         // the update's operands, read while the decay scan below runs
