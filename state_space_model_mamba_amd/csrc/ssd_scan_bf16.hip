@@ -949,11 +949,11 @@ struct StCursor {
 // tile_words on a byte address and a 32-bit row count.
 // (the clamp is written out as scalar min and max: as C, the compiler folds
 // it into a vector median, and the products after it then run on the vector
-// unit too)
+// unit too.  Both instructions write SCC, which the statement declares.)
 __device__ __forceinline__ u32x4 tile_words32(uint64_t p, int rows, unsigned pitch, unsigned row_bytes)
 {
     int r;
-    asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(rows), "n"(kT));
+    asm("s_max_i32 %0, %1, 0\n\ts_min_i32 %0, %0, %2" : "=&s"(r) : "s"(rows), "n"(kT) : "scc");
     const int bytes = r * (int)pitch - (int)pitch + (int)row_bytes;
     u32x4 d;
     d.x = __builtin_amdgcn_readfirstlane((unsigned)p);
