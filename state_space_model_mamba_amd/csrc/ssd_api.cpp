@@ -294,7 +294,7 @@ struct GroupModel {
                 return m.second;
         const ssd::Bf16Plan p = ssd::plan_scan_bf16(grp[r].B, grp[r].L, d->nheads, d->ngroups,
                                                     d->chunk, run_cus(grp[r], total), nseg, false);
-        const int64_t seg_tok = p.chunks_per_seg * d->chunk;
+        const int64_t seg_tok = p.seg_tokens;
         const SegShape sh{p.nseg, seg_tok, grp[r].L - (p.nseg - 1) * seg_tok, p.nsub};
         memo[r].push_back({nseg, sh});
         return sh;
@@ -802,7 +802,7 @@ SSD_EXPORT ssd_status ssd_chunk_scan_varlen(const ssd_dims *dims, const int64_t 
         for (size_t r = 0; r < order.size(); ++r)
             order[r] = r;
         std::stable_sort(order.begin(), order.end(), [&](size_t a, size_t b) {
-            return plans[a].chunks_per_seg * dims->chunk > plans[b].chunks_per_seg * dims->chunk;
+            return plans[a].seg_tokens > plans[b].seg_tokens;
         });
         ssd::Bf16Run runs[ssd::kMaxRuns];
         char *wsp = static_cast<char *>(workspace);

@@ -108,7 +108,8 @@ hipError_t launch_scan_f32(int64_t B, int64_t L, int64_t H, int64_t P, int64_t N
 struct Bf16Plan {
     int64_t nchunks;       // ceil(L / Q)
     int64_t quads;         // work-groups per (batch row, segment): G * ceil(H / G / 4)
-    int64_t chunks_per_seg;
+    int64_t chunks_per_seg;  // ceil(seg_tokens / Q), for reports
+    int64_t seg_tokens;    // tokens per segment (a multiple of 64; the last may be shorter)
     int64_t nseg;          // segments per (b, h) of the scan kernel
     int64_t nsub;          // state-kernel units per segment (each segment but the last)
     int64_t unit_tokens;   // tokens per unit (a multiple of 64)

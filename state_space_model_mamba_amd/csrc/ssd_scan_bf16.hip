@@ -121,7 +121,7 @@ struct SegArgs {
     int H, G;
     int hg;              // heads per group
     int nq;              // work-groups (head quads) per group
-    int64_t seg_tokens;  // tokens per segment (whole chunks)
+    int64_t seg_tokens;  // tokens per segment (whole 64-token tiles)
     int64_t unit_tokens; // tokens per state-kernel unit
     int nseg;            // segments per (b, h)
     int nsub;            // state-kernel units per segment
@@ -1263,32 +1263,37 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, i
     // state work-groups per segment, and how many fit on the chip at once (LDS)
     const int64_t per_seg1 = std::max<int64_t>(1, B * G * ((hg + kStHeads - 1) / kStHeads));
     const int64_t slots1 = kCUs * (int64_t)(160 * 1024 / kStSmemBytes);
-    // Segments per sequence.  The scan kernel runs one work-group per CU, so its
-    // time is ~ rounds * chunks per segment; the state kernel (about half the
-    // work per tile) re-reads x for all but the last segment, and every segment
-    // adds state traffic through the workspace.
+    // Segments per sequence, in whole 64-token tiles (the kernels' step; the
+    // result does not depend on where the segments end).  The scan kernel runs
+    // one work-group per CU, so its time is ~ rounds * tiles per segment; the
+    // state kernel (about half the work per tile) re-reads x for all but the
+    // last segment, and every segment adds state traffic through the
+    // workspace (about two tiles' worth).
+    const int64_t tiles = std::max<int64_t>(1, (L + kT - 1) / kT);
     int64_t nseg = use_env ? env_int("SSD_NSEG", 0) : 0;
     if (nseg <= 0)
         nseg = nseg_fixed;
     if (nseg <= 0) {
         double best = 1e300;
-        for (int64_t k = 1; k <= std::max<int64_t>(p.nchunks, 1); ++k) {
-            const int64_t cps = (p.nchunks + k - 1) / k;
-            const int64_t ns = (p.nchunks + cps - 1) / cps;
+        for (int64_t k = 1; k <= tiles; ++k) {
+            const int64_t tps = (tiles + k - 1) / k;
+            const int64_t ns = (tiles + tps - 1) / tps;
             if (ns != k)
                 continue;
             const double r3 = (double)((per_seg * ns + kCUs - 1) / kCUs);
             const double r1 = (double)((per_seg1 * (ns - 1) + slots1 - 1) / slots1);
-            const double cost = (r3 + 0.5 * r1) * (double)cps + 0.5 * (double)ns;
+            const double cost = (r3 + 0.5 * r1) * (double)tps + 2.0 * (double)ns;
             if (cost < best) {
                 best = cost;
                 nseg = ns;
             }
         }
     }
-    nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, std::max<int64_t>(p.nchunks, 1)));
-    p.chunks_per_seg = std::max<int64_t>(1, (p.nchunks + nseg - 1) / nseg);
-    p.nseg = std::max<int64_t>(1, (p.nchunks + p.chunks_per_seg - 1) / p.chunks_per_seg);
+    nseg = std::max<int64_t>(1, std::min<int64_t>(nseg, tiles));
+    const int64_t seg_tiles = (tiles + nseg - 1) / nseg;
+    p.seg_tokens = seg_tiles * kT;
+    p.nseg = (tiles + seg_tiles - 1) / seg_tiles;
+    p.chunks_per_seg = (p.seg_tokens + Q - 1) / Q;
     // The state kernel may cut each of its segments into units to fill the
     // chip; every unit adds one more state to write, and the scan kernel's
     // last segment chains (nseg-1) * nsub states before its first tile.  Cost
@@ -1297,9 +1302,8 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, i
     // tile costs a work-group ~1.9 us when few run, and their HBM traffic
     // (~49 KB per tile and work-group) caps a round at ~5 TB/s; each chained
     // unit state adds ~2.75 us to the scan kernel's prologue.
-    const int64_t seg_tiles = p.chunks_per_seg * Q / kT;
     p.nsub = 1;
-    p.unit_tokens = p.chunks_per_seg * Q;
+    p.unit_tokens = p.seg_tokens;
     if (p.nseg > 1) {
         constexpr double kTileUs = 1.9, kChainUs = 2.75, kHbmBytesPerUs = 5.0e6;
         constexpr double kTileBytes = (double)kT * (kStHeads * kP * 2 + kN * 2 + kStHeads * 4);
@@ -1352,7 +1356,7 @@ SegArgs seg_args(const Bf16Plan &plan, int64_t B, int64_t L, int64_t H, int64_t 
     a.H = (int)H;
     a.G = (int)G;
     a.hg = (int)(H / G);
-    a.seg_tokens = plan.chunks_per_seg * Q;
+    a.seg_tokens = plan.seg_tokens;
     a.unit_tokens = plan.unit_tokens;
     a.nseg = (int)plan.nseg;
     a.nsub = (int)plan.nsub;
