@@ -103,6 +103,7 @@ template <int kH> struct __align__(16) ScanSmem {
     float lam[kWaves][kT];                    // log2(e) Lam_s, tile-referenced
     float dtv[kWaves][kT];                    // dt_s (0 past the end)
     float vt[kWaves][kT];                     // exp(Lam_q - Lam_s) dt_s, q = last token of s's 16-block
+    float gt[kWaves][kT];                     // exp(Lam_t - Lam_p), p = last token of the 16-block before t's
     float wd[kWaves][kT];                     // dt_s 2^(bias - log2(e) Lam_s), see stage_tile
 };
 struct SegArgs {
@@ -402,6 +403,7 @@ __device__ __forceinline__ bool uniform(bool v)
 
 struct TileMode {
     float ly;       // ls of the state entering the tile (decay of Y_off)
+    float eyl;      // 2^ly
     float zscale;   // direct mode: Z <- zscale Z + update
     bool direct;
     bool renorm;    // before the tile: Z <- rscale Z
@@ -428,6 +430,7 @@ __device__ __forceinline__ TileMode tile_mode(float lam_end, float &ls, float &l
     md.zscale = direct ? fast_exp2(ls + lam_end) : 1.f;
     bias = direct ? lam_end : -ls_in;
     ls = direct ? 0.f : ls_in + lam_end;
+    md.eyl = fast_exp2(md.ly);
     return md;
 }
 
@@ -518,7 +521,7 @@ __device__ __forceinline__ void state_update_pre(f32x4 (&Z)[8][2], const bf16x8 
 // between this and the tile, so the tables of tile k + 1 can be formed while
 // tile k is computed.
 struct Tables {
-    float lam, dtv, vt, wd;
+    float lam, dtv, vt, wd, gt;
     TileMode md;
 };
 template <bool kNested = true>
@@ -543,6 +546,10 @@ __device__ __forceinline__ Tables tile_tables(float dtl, int64_t t0, int64_t L, 
     tb.lam = lam;
     tb.dtv = dtl;
     tb.vt = fast_exp2(lq - lam) * dtl;
+    // the decay from the end of the previous 16-token block (Lam = 0 before
+    // the tile): every factor of the tile's row decays is a product of these
+    const float lp = row == 0 ? 0.f : row == 1 ? q0 : row == 2 ? q1 : q2;
+    tb.gt = fast_exp2(lam - lp);
     return tb;
 }
 
@@ -570,6 +577,7 @@ __device__ __forceinline__ void stage_tile(ScanSmem<kH> &sm, Prefetch<kH> &pf, i
     sm.lam[w][l] = tb.lam;
     sm.dtv[w][l] = tb.dtv;
     sm.vt[w][l] = tb.vt;
+    sm.gt[w][l] = tb.gt;
 }
 
 // The fused step-size prep on a prefetched tile at t0 (lane = token): the
@@ -727,11 +735,22 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                         Y[q][tb] = mfma32(za, CF[tb], kk == 0 ? zero4 : Y[q][tb]);
                 }
             }
-            float lamt[4];
+            // Row decays 2^(Lam_t + ly) and the off-diagonal factors
+            // 2^(Lam_t - Lam_q(sb)) as products of the tables' block decays
+            // (all factors at most 1): pt = 2^(Lam_t - Lam_p) for t's row,
+            // bj = the decay across block j, eb = 2^(Lam_p + ly).
+            float lamt[4], pt[4];
+            const float b1 = sm.gt[w][31], b2 = sm.gt[w][47];
+            float eb[4];
+            eb[0] = md.eyl;
+            eb[1] = eb[0] * sm.gt[w][15];
+            eb[2] = eb[1] * b1;
+            eb[3] = eb[2] * b2;
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
                 lamt[tb] = sm.lam[w][16 * tb + c];
-                const float dec = fast_exp2(lamt[tb] + md.ly);
+                pt[tb] = sm.gt[w][16 * tb + c];
+                const float dec = pt[tb] * eb[tb];
 #pragma unroll
                 for (int q = 0; q < 2; ++q)
                     Y[q][tb] *= dec;
@@ -755,7 +774,9 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                         const int sb = 2 * jj + hh;
                         f32x4 v = zero4;
                         if (sb < tb) {
-                            const float u = fast_exp2(lamt[tb] - sm.lam[w][16 * sb + 15]);
+                            // 2^(Lam_t - Lam_q(sb)): blocks sb + 1 .. tb - 1 lie between
+                            const float u = sb + 1 == tb ? pt[tb] : sb + 2 == tb ? pt[tb] * (tb == 2 ? b1 : b2)
+                                                                                 : pt[tb] * (b1 * b2);
                             const f32x4 vt = *reinterpret_cast<const f32x4 *>(&sm.vt[w][16 * sb + 4 * g]);
                             v = sm.Gs[gblock(sb, tb)][l] * (vt * u);
                         } else if (sb == tb) {
