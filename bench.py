@@ -1011,9 +1011,9 @@ def main():
         if 256 in args.decode_batches:
             extra["gdn_decode"] = bench_gdn(args)
             progress("gdn decode")
-    configs = {}
+    others = {}
     for v in secondary:
-        configs[v] = prefill_line(bench_prefill(args, v, resident[v], steps=max(args.steps // 2, 5),
+        others[v] = prefill_line(bench_prefill(args, v, resident[v], steps=max(args.steps // 2, 5),
                                                 warmup=max(args.warmup, 5)), v)
         del resident[v]
         progress(f"prefill {v}")
@@ -1044,8 +1044,8 @@ def main():
         "roofline_step": pre["roofline_step"],
         "mfma": pre["mfma"],
     }
-    if configs:
-        line["prefill_configs"] = configs
+    if others:
+        line["prefill_configs"] = others
     if not args.no_extras:
         line["prefill_fused_dt_softplus"] = dict(
             pre["dt_softplus"],
