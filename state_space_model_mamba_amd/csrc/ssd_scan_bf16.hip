@@ -845,11 +845,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
         update_state(Bs, XS, md);
     };
 
-    // Tile k is staged in ring slot k & 1 (B, C, x) and in the wave's own
-    // tables; tile k + 1's loads are in flight in `pf` while tile k is
-    // computed.  The barrier at the top of an iteration publishes the slot
-    // written at the end of the previous one and guarantees every wave is done
-    // reading the slot the current iteration will overwrite.
+    // Z <- 2^ls Z, ls restarting at 0, before a tile that would take ls below
+    // -kRenorm (a uniform branch)
     auto renorm = [&](const TileMode &md) {
         if (uniform(md.renorm)) {
 #pragma unroll
