@@ -600,6 +600,12 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
     constexpr int kHeads = kH, kWaves = 2 * kH;
     const int tid = threadIdx.x, w = wave_id(), l = tid & 63, g = l >> 4, c = l & 15;
     const int hs = w >> 1;                                // head slot in the work-group
+    // One wave of each pair that shares a SIMD (w and w + 4, or 2k and 2k + 1:
+    // the even-parity wave indices 0, 3, 5, 6 hold one of each either way)
+    // takes issue priority from the mid-tile barrier until its masked-operand
+    // product is issued, so that the pair's VALU-bound masked-operand builds
+    // and MFMA-bound products drift apart instead of running side by side.
+    const bool lead = (__builtin_popcount(w) & 1) == 0;
     const int ph = w & 1;                                 // P half: p = 32 ph .. 32 ph + 31
     const int64_t j = xcd_remap(bid, nblk);
     const int nquad = a.G * a.nq;
@@ -756,6 +762,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                     Y[q][tb] *= dec;
             }
             lds_barrier();                            // every block of the tile is in Gs
+            if (lead)
+                __builtin_amdgcn_s_setprio(2);
             // the next tile's step sizes and decay tables, well before they
             // are staged at the end of this tile
             prep_dt<kH, kSp>(pf, t0 + kT, tseg1, dtb, l);
@@ -840,6 +848,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                 __builtin_amdgcn_raw_buffer_store_b128(v, ry, ylane + 32u * tb * (unsigned)ystride, 0, 0);
             }
         }
+        if (lead)
+            __builtin_amdgcn_s_setprio(0);
         bf16x8 XS[2][2];
         scale_x(XS, XT, sm.wd[w], g);
         update_state(Bs, XS, md);
