@@ -698,6 +698,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
         const unsigned char *Xs = sm.Xt[slot][hs];
         const unsigned char *Bs = sm.Bt[slot];
         bf16x8 XT[2][2];      // x^T: rows p (this wave's half), K over tokens
+        bf16x8 XS[2][2];      // x^T scaled by the update weights
         {
             const unsigned char *Cs = sm.Ct[slot];
             // (C B^T)^T causal blocks, shared by the four heads: wave w computes
@@ -827,6 +828,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
             // descriptor is empty.  The stores are issued on every path: under a
             // branch, the wait for the next tile's loads in stage_tile would also
             // wait for these stores to complete.
+            // the update's operand, formed while the products above run
+            scale_x(XS, XT, sm.wd[w], g);
             const rsrc_t ry = tile_rsrc(ybase + t0 * ystride, active ? L - t0 : 0, (unsigned)ystride * 2u, kP * 2);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
@@ -850,8 +853,6 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
         }
         if (lead)
             __builtin_amdgcn_s_setprio(0);
-        bf16x8 XS[2][2];
-        scale_x(XS, XT, sm.wd[w], g);
         update_state(Bs, XS, md);
     };
 
