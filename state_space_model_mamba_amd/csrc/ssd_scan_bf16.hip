@@ -175,15 +175,10 @@ __device__ __forceinline__ float lane_f(float v, int lane)
 {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
-// kNested: the earlier rows' totals as one nested select, which the compiler
-// turns into divergent branches; otherwise as three independent selects (no
-// branch).  Each row adds the same terms in the same order either way.  The
-// state kernel takes the selects (1.5-2.5 us faster); the plain scan kernel
-// keeps the nested form, which measured 2-5 us faster there in its tables of
-// the next tile (formed mid-tile, where the branches also bound how far the
-// scheduler moves that chain), while the fused-softplus scan kernel, whose
-// chain starts with the softplus, is 2-3 us faster with the selects.
-template <bool kNested = false>
+// Inclusive prefix sum over the wave's 64 lanes: DPP shifts within each
+// 16-lane row, then the earlier rows' totals added as three independent
+// selects (no branch; a nested select became divergent branches on this
+// dependent chain).
 __device__ __forceinline__ float wave_inclusive_sum(float v, int lane)
 {
     v += dpp_row_shr<0x111>(v);   // row_shr:1
@@ -192,10 +187,7 @@ __device__ __forceinline__ float wave_inclusive_sum(float v, int lane)
     v += dpp_row_shr<0x118>(v);   // row_shr:8
     const float r0 = lane_f(v, 15), r1 = lane_f(v, 31), r2 = lane_f(v, 47);
     const int row = lane >> 4;
-    if constexpr (kNested)
-        return v + (row == 0 ? 0.f : row == 1 ? r0 : row == 2 ? r0 + r1 : r0 + r1 + r2);
-    else
-        return v + (((row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f)) + (row >= 3 ? r2 : 0.f));
+    return v + (((row >= 1 ? r0 : 0.f) + (row >= 2 ? r1 : 0.f)) + (row >= 3 ? r2 : 0.f));
 }
 
 // K-major MFMA operand from a token-major LDS tile with gfx950's transpose read
@@ -524,12 +516,11 @@ struct Tables {
     float lam, dtv, vt, wd, gt;
     TileMode md;
 };
-template <bool kNested = true>
 __device__ __forceinline__ Tables tile_tables(float dtl, int64_t t0, int64_t L, float Ah2, float &ls,
                                               float &lsum, int l)
 {
     Tables tb;
-    const float lam = wave_inclusive_sum<kNested>(dtl * Ah2, l);
+    const float lam = wave_inclusive_sum(dtl * Ah2, l);
     // Lam at the last valid token (in a ragged tile the zero-dt lanes after it
     // hold the same sum only up to the summation order, which matters when
     // the decay is extreme and Lam is large)
@@ -768,7 +759,7 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
             // the next tile's step sizes and decay tables, well before they
             // are staged at the end of this tile
             prep_dt<kH, kSp>(pf, t0 + kT, tseg1, dtb, l);
-            tnext = tile_tables<!kSp>(pf.dt, t0 + kT, tseg1, Ah2, ls, lsum, l);
+            tnext = tile_tables(pf.dt, t0 + kT, tseg1, Ah2, ls, lsum, l);
             // Mask and decay, B-operand over tokens s (slot 4 h + i <-> s = 32 jj + 16 h + 4 g + i):
             //   s in an earlier 16-block: exp(Lam_t - Lam_q) * [exp(Lam_q - Lam_s) dt_s]
             //   s in t's 16-block      : exp(Lam_t - Lam_s) dt_s for s <= t (exponent
