@@ -810,6 +810,8 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
                     if (tb >= 2)
                         Y[q][tb] = mfma32(XT[q][1], MOP[tb][1], Y[q][tb]);
                 }
+            // the update's operand, formed while the products above run
+            scale_x(XS, XT, sm.wd[w], g);
             // Lane (c, g) holds columns 16 q + 4 g .. +3 (q = 0, 1) of the wave's
             // half of row 16 tb + c.  Swapping the upper and lower 32 lanes of the
             // q = 1 and q = 0 registers, then the odd and even 16-lane rows, leaves
@@ -819,8 +821,6 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
             // descriptor is empty.  The stores are issued on every path: under a
             // branch, the wait for the next tile's loads in stage_tile would also
             // wait for these stores to complete.
-            // the update's operand, formed while the products above run
-            scale_x(XS, XT, sm.wd[w], g);
             const rsrc_t ry = tile_rsrc(ybase + t0 * ystride, active ? L - t0 : 0, (unsigned)ystride * 2u, kP * 2);
 #pragma unroll
             for (int tb = 0; tb < 4; ++tb) {
