@@ -593,9 +593,10 @@ __device__ __forceinline__ void scan_body(const SegArgs &a, ScanSmem<kH> &sm, in
     const int hs = w >> 1;                                // head slot in the work-group
     // One wave of each pair that shares a SIMD (w and w + 4, or 2k and 2k + 1:
     // the even-parity wave indices 0, 3, 5, 6 hold one of each either way)
-    // takes issue priority from the mid-tile barrier until its masked-operand
-    // product is issued, so that the pair's VALU-bound masked-operand builds
-    // and MFMA-bound products drift apart instead of running side by side.
+    // takes issue priority from the mid-tile barrier until its y stores are
+    // issued (before the state update), so that the pair's VALU-bound
+    // masked-operand builds and MFMA-bound products drift apart instead of
+    // running side by side.
     const bool lead = (__builtin_popcount(w) & 1) == 0;
     const int ph = w & 1;                                 // P half: p = 32 ph .. 32 ph + 31
     const int64_t j = xcd_remap(bid, nblk);
