@@ -360,11 +360,33 @@ def bench_prefill(args, wname, t, steps=None, warmup=None, extras=False):
                 marks.append((a, b))
         torch.cuda.synchronize()
         per_blk = [a.elapsed_time(b) / blk for a, b in marks]
-        plain_ms, sp_ms = float(np.median(per_blk[0::2])), float(np.median(per_blk[1::2]))
+        blk_plain, blk_sp = float(np.median(per_blk[0::2])), float(np.median(per_blk[1::2]))
+        # sustained: each form runs warm, 10 untimed calls ahead of a block of
+        # `long` timed ones, the two forms still alternating; short blocks
+        # above charge every switch between the two kernel instantiations to
+        # the block after it
+        long, lp, lf = max(20, min(steps, 100)), [], []
+        for _ in range(rounds):
+            for fn, acc in ((step, lp), (fused, lf)):
+                for _ in range(10):
+                    fn()
+                a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                a.record()
+                for _ in range(long):
+                    fn()
+                b.record()
+                torch.cuda.synchronize()
+                acc.append(a.elapsed_time(b) / long)
+        plain_ms, sp_ms = float(np.median(lp)), float(np.median(lf))
         sp = {"event_ms_per_step": sp_ms, "plain_event_ms_per_step": plain_ms,
               "overhead_pct": 100.0 * (sp_ms / plain_ms - 1.0),
-              "timing": f"{rounds} alternating pairs of {blk}-step blocks (plain, fused), "
-                        "queued back to back; medians of the blocks"}
+              "timing": f"{rounds} alternating pairs of {long}-step blocks (plain, fused), each "
+                        "after 10 untimed calls of its own form; medians of the blocks",
+              "short_blocks": {"overhead_pct": 100.0 * (blk_sp / blk_plain - 1.0),
+                               "event_ms_per_step": blk_sp, "plain_event_ms_per_step": blk_plain,
+                               "timing": f"{rounds} alternating pairs of {blk}-step blocks, "
+                                         "queued back to back (each block pays the switch from "
+                                         "the other form); medians of the blocks"}}
     nbytes = prefill_bytes(w)
     flops = prefill_useful_flops(w)
     k3 = kern["chunk_scan_kernel"]

@@ -24,17 +24,17 @@ def inputs(w):
     return inp, A, D, g
 
 
-def both(w, g, h0=None, in_place=False):
+def both(w, g, h0=None, in_place=False, **kw):
     """(y, state) of ssd_chunk_scan with its own workspace and of the no-alloc
     entry point (outputs passed in: nothing is allocated around the call)."""
     args = (g["x"], g["dt"], g["A"], g["B"], g["C"], g["D"], w.chunk)
     init1 = None if h0 is None else dev(h0)
     y1, s1 = ssd.ssd_chunk_scan(*args, initial_state=init1,
-                                final_state=init1 if in_place else None)
+                                final_state=init1 if in_place else None, **kw)
     init2 = None if h0 is None else dev(h0)
     y2 = torch.empty_like(g["x"])
     s2 = init2 if in_place else torch.empty((w.batch, w.nheads, 64, 128), device="cuda")
-    out = ssd.ssd_chunk_scan_noalloc(*args, initial_state=init2, y=y2, final_state=s2)
+    out = ssd.ssd_chunk_scan_noalloc(*args, initial_state=init2, y=y2, final_state=s2, **kw)
     torch.cuda.synchronize()
     assert out[0] is y2 and out[1] is s2
     return host(y1), host(s1), host(y2), host(s2)
@@ -74,6 +74,27 @@ def test_noalloc_matches_scan_on_consecutive_calls():
     y1, s1, y2, s2 = both(big, g0)
     assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
     against_oracle(big, inp_b, A_b, np.zeros_like(D_b), None, y2, s2)
+
+
+def test_noalloc_fused_step_sizes():
+    """With the fused step-size prep (u in place of dt, the step sizes formed
+    inside the kernels): the same results as ssd_chunk_scan with its own
+    workspace, on a fused call between two plain ones over the same scratch
+    array, and the oracle's tolerance on the fp64 step sizes."""
+    w = si.small_workload(batch=2, seqlen=3000, nheads=8, ngroups=2, chunk=256, seed=305)
+    inp, A, D, g = inputs(w)
+    u = np.random.default_rng(306).uniform(-8.0, -2.0, inp["dt"].shape).astype(np.float32)
+    bias = np.random.default_rng(307).uniform(-0.5, 1.0, 8).astype(np.float32)
+    gu = dict(g, dt=dev(u))
+    y1, s1, y2, s2 = both(w, g)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+    y1, s1, y2, s2 = both(w, gu, dt_softplus=True, dt_bias=dev(bias))
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
+    ref = dict(inp)
+    ref["dt"] = oracle.dt_softplus(u, bias).astype(np.float32)
+    against_oracle(w, ref, A, D, None, y2, s2)
+    y1, s1, y2, s2 = both(w, g)
+    assert np.array_equal(y1, y2) and np.array_equal(s1, s2)
 
 
 def test_noalloc_without_workspace_need():
