@@ -1288,22 +1288,29 @@ Bf16Plan plan_scan_bf16(int64_t B, int64_t L, int64_t H, int64_t G, int64_t Q, i
     // result does not depend on where the segments end).  The scan kernel runs
     // one work-group per CU, so its time is ~ rounds * tiles per segment; the
     // state kernel (about half the work per tile) re-reads x for all but the
-    // last segment, and every segment adds state traffic through the
-    // workspace (about two tiles' worth).
+    // last segment, and every segment adds one unit state, which the last
+    // segment's work-groups chain before their first tile (~2.75 us, 0.6 of a
+    // tile at the 2.7B layer) and which passes through the workspace: about a
+    // tile's worth.  When the scan fits one round of work-groups, only such
+    // plans are taken: a second round measured slower than this cost says
+    // (131072 tokens, 80 heads in 8 groups: 21 segments 1.39 ms, 10 segments
+    // 1.33 ms), while within one round more segments paid (the 130M-shaped
+    // layer: 5 segments 63.3 us, 4 segments 70.0 us).
     const int64_t tiles = std::max<int64_t>(1, (L + kT - 1) / kT);
     int64_t nseg = use_env ? env_int("SSD_NSEG", 0) : 0;
     if (nseg <= 0)
         nseg = nseg_fixed;
     if (nseg <= 0) {
+        const bool one_round = per_seg <= kCUs;
         double best = 1e300;
         for (int64_t k = 1; k <= tiles; ++k) {
             const int64_t tps = (tiles + k - 1) / k;
             const int64_t ns = (tiles + tps - 1) / tps;
-            if (ns != k)
+            if (ns != k || (one_round && per_seg * ns > kCUs))
                 continue;
             const double r3 = (double)((per_seg * ns + kCUs - 1) / kCUs);
             const double r1 = (double)((per_seg1 * (ns - 1) + slots1 - 1) / slots1);
-            const double cost = (r3 + 0.5 * r1) * (double)tps + 2.0 * (double)ns;
+            const double cost = (r3 + 0.5 * r1) * (double)tps + 1.0 * (double)ns;
             if (cost < best) {
                 best = cost;
                 nseg = ns;
