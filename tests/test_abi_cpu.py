@@ -312,3 +312,19 @@ def test_noalloc_rejects_workspace_beyond_scratch(lib):
     d.headdim = 32
     assert lib.ssd_chunk_scan_noalloc(ctypes.byref(d), *p, None) == 3
     assert lib.ssd_chunk_scan_noalloc(None, *p, None) == 1
+
+
+def test_planner_segment_counts(lib):
+    """The planner's segment counts at the three layer shapes, read back from
+    the workspace size (one state slot per unit of the first nseg - 1 segments,
+    one unit each at these shapes, plus one spare: B*H*nseg*P*N*4 bytes plus
+    the slots' decays, each part 256-byte aligned).  2.7B layer: 3 segments
+    (240 scan work-groups); 130M layer: 5 (240); 131072 tokens in 8 groups: 10
+    (240, the one-round maximum: 21 segments, a two-round plan, measured
+    slower)."""
+    def align(n):
+        return (n + 255) // 256 * 256
+    for (b, L, H, G, nseg) in ((4, 8192, 80, 1, 3), (8, 2048, 24, 1, 5), (1, 131072, 80, 8, 10)):
+        slots = b * H * nseg
+        want = align(slots * 64 * 128 * 4) + align(slots * 4)
+        assert ssd.ssd_chunk_scan_workspace_size(b, L, H, 64, 128, G, 256) == want, (b, L, H, G)
