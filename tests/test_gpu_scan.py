@@ -111,6 +111,37 @@ def test_m2_2p7b_sampled_heads():
     assert np.all(np.isfinite(yh)) and np.all(np.isfinite(sh))
 
 
+@pytest.mark.parametrize("batch,L,nseg", [(16, 700, 1), (13, 1500, 4)])
+def test_multi_round_default_plan(batch, L, nseg):
+    """Batches whose scan work-groups per segment (batch x 20 head quads) exceed
+    the 256 CUs, so no plan fits one round and the planner's cost picks among
+    multi-round plans: 16 x 700 tokens in one segment (320 work-groups, two
+    rounds, no state kernel); 13 x 1500 tokens in 4 segments (1040 scan and
+    780 state work-groups, several rounds of each).  The segment count is read
+    back from the workspace size; 16 sampled (b, h) sequences, the last row
+    and head among them, against the oracle, with and without D."""
+    w = si.small_workload(batch=batch, seqlen=L, nheads=80, ngroups=1, chunk=256, seed=L + batch)
+    need = ssd.ssd_chunk_scan_workspace_size(batch, L, 80, 64, 128, 1, 256)
+    slots = batch * 80 * nseg if nseg > 1 else 0
+    assert need == ((slots * 64 * 128 * 4 + 255) // 256 * 256 + (slots * 4 + 255) // 256 * 256
+                    if slots else 0)
+    inp = si.prefill_inputs(w)
+    g, A, D = gpu_inputs(w, inp)
+    y, s = gpu_scan(g, w.chunk)
+    y0, s0 = gpu_scan(g, w.chunk, D=torch.zeros_like(g["D"]))
+    assert torch.equal(s, s0), "the state does not depend on D"
+    pairs = sorted(set(sample_pairs(batch, 80, 14, seed=L) + [(0, 0), (batch - 1, 79)]))
+    yref, sref = oracle_heads(inp, w.io, A, D, pairs)
+    yref0, _ = oracle_heads(inp, w.io, A, np.zeros_like(D), pairs)
+    yh, y0h, sh = host(y), host(y0), host(s)
+    tol = TOL[w.io]
+    for i, (b, h) in enumerate(pairs):
+        assert rel(yh[b, :, h], yref[i]) <= tol, (b, h, rel(yh[b, :, h], yref[i]))
+        assert rel(y0h[b, :, h], yref0[i]) <= tol, (b, h, rel(y0h[b, :, h], yref0[i]))
+        assert rel(sh[b, h], sref[i]) <= tol, (b, h, rel(sh[b, h], sref[i]))
+    assert np.all(np.isfinite(yh)) and np.all(np.isfinite(sh))
+
+
 def test_longctx_prefix_fullrun_and_decode_continuity():
     """131072 tokens, 8 groups: (1) the [0, 4096) prefix as its own scan against
     the oracle; (2) the full-length scan on 8 sampled heads against the oracle's
